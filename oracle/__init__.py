@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for the attention hot path — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. The product path (the HIP library and its binding) never does.
+
+The arithmetic lives in ``oracle.c`` (plain loops, fp64, one definition per
+operation); this module only builds it with gcc and marshals numpy arrays.
+Every function here is pinned by the ``-m "not gpu"`` tests against
+independent facts (brute force, library routines, closed forms, invariants,
+printed numbers); see ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-std=c11", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, f64 = ctypes.c_int32, ctypes.c_double
+        L.oracle_packed_prefill.argtypes = [P, P, P, P, i32, i32, i32, i32, f64, P, P, i32]
+        L.oracle_shared_prefix_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                  f64, P, P, i32]
+        L.oracle_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32]
+        L.oracle_beam_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
+        L.oracle_num_threads.argtypes = [i32]
+        for f in (L.oracle_packed_prefill, L.oracle_shared_prefix_decode, L.oracle_suffix_reorder,
+                  L.oracle_beam_topk, L.oracle_num_threads):
+            f.restype = i32
+        _lib = L
+    return _lib
+
+
+def _bits(a) -> np.ndarray:
+    """bf16 input as a contiguous uint16 array (accepts numpy uint16 or a torch bf16 tensor)."""
+    if hasattr(a, "dtype") and str(a.dtype) == "torch.bfloat16":
+        import torch
+        a = a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("expected bf16 bits as uint16")
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads(requested: int = 0) -> int:
+    return int(lib().oracle_num_threads(requested))
+
+
+def packed_prefill(q, k, v, cu_seqlens, scale=None, nthreads: int = 0):
+    """fp64 (out [T,Nq,D], lse [T,Nq]) of packed causal GQA prefill."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    t, nq, d = q.shape
+    nkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((t, nq, d), np.float64)
+    lse = np.zeros((t, nq), np.float64)
+    rc = lib().oracle_packed_prefill(_p(q), _p(k), _p(v), _p(cu), len(cu) - 1, nq, nkv, d, float(scale),
+                                     _p(out), _p(lse), nthreads)
+    if rc:
+        raise ValueError(f"oracle_packed_prefill rejected its arguments ({rc})")
+    return out, lse
+
+
+def shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, suffix_len, scale=None, nthreads: int = 0):
+    """fp64 (out [R,W,Nq,D], lse [R,W,Nq]) of shared-prefix decode over [prefix; suffix[:suffix_len]]."""
+    q, pk, pv = _bits(q), _bits(prefix_k), _bits(prefix_v)
+    sk, sv = _bits(suffix_k), _bits(suffix_v)
+    r, w, nq, d = q.shape
+    lp, nkv = pk.shape[1], pk.shape[2]
+    ls_cap = sk.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((r, w, nq, d), np.float64)
+    lse = np.zeros((r, w, nq), np.float64)
+    rc = lib().oracle_shared_prefix_decode(_p(q), _p(pk), _p(pv), _p(sk), _p(sv), r, w, lp, suffix_len, ls_cap,
+                                           nq, nkv, d, float(scale), _p(out), _p(lse), nthreads)
+    if rc:
+        raise ValueError(f"oracle_shared_prefix_decode rejected its arguments ({rc})")
+    return out, lse
+
+
+def suffix_reorder(src_k, src_v, parent, suffix_len, src_tokens=None, num_tokens=0):
+    """Gathered copies (dst_k, dst_v[, dst_tokens]) ; positions >= suffix_len are left zero."""
+    sk, sv = _bits(src_k), _bits(src_v)
+    r, w, ls_cap, nkv, d = sk.shape
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    dk, dv = np.zeros_like(sk), np.zeros_like(sv)
+    st = dt = None
+    tok_cap = 0
+    if src_tokens is not None:
+        st = np.ascontiguousarray(src_tokens, dtype=np.int32)
+        tok_cap = st.shape[2]
+        dt = np.zeros_like(st)
+    rc = lib().oracle_suffix_reorder(_p(sk), _p(sv), _p(dk), _p(dv), _p(par), _p(st), _p(dt), r, w, suffix_len,
+                                     ls_cap, nkv, d, num_tokens, tok_cap)
+    if rc:
+        raise ValueError(f"oracle_suffix_reorder rejected its arguments ({rc})")
+    return (dk, dv) if st is None else (dk, dv, dt)
+
+
+def beam_topk(logits, cum, k_local, k_global, nthreads: int = 0):
+    """Two-stage selection. Returns a dict of numpy arrays:
+    tokens/parents/scores [R,k_global], local_tokens/local_scores [R,W_in,k_local],
+    row_lse (fp32) and row_lse64 [R,W_in]."""
+    x = _bits(logits)
+    r, w_in, vocab = x.shape
+    c = None if cum is None else np.ascontiguousarray(cum, dtype=np.float32)
+    out = dict(
+        tokens=np.zeros((r, k_global), np.int32), parents=np.zeros((r, k_global), np.int32),
+        scores=np.zeros((r, k_global), np.float32),
+        local_tokens=np.zeros((r, w_in, k_local), np.int32), local_scores=np.zeros((r, w_in, k_local), np.float32),
+        row_lse=np.zeros((r, w_in), np.float32), row_lse64=np.zeros((r, w_in), np.float64),
+    )
+    rc = lib().oracle_beam_topk(_p(x), _p(c), r, w_in, vocab, k_local, k_global, _p(out["tokens"]),
+                                _p(out["parents"]), _p(out["scores"]), _p(out["local_tokens"]),
+                                _p(out["local_scores"]), _p(out["row_lse"]), _p(out["row_lse64"]), nthreads)
+    if rc:
+        raise ValueError(f"oracle_beam_topk rejected its arguments ({rc})")
+    return out
