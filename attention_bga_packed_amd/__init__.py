@@ -1,0 +1,19 @@
+"""attention_bga_packed_amd — the attention hot path of a bounded-generation
+SLM engine (packed causal GQA prefill, shared-prefix beam decode, parent-index
+reorder, two-stage beam top-K) as HIP kernels for MI355X (gfx950) behind the C
+ABI in include/bga.h.
+
+Importing the package loads libbga.so and raises if it is missing; there is no
+fallback path.
+"""
+from ._binding import (  # noqa: F401
+    BgaError,
+    EXPORTS,
+    LIB_PATH,
+    beam_topk,
+    beam_topk_workspace_size,
+    lib,
+    packed_gqa_prefill,
+    shared_prefix_decode,
+    suffix_reorder,
+)

@@ -1,0 +1,211 @@
+"""Thin ctypes binding of libbga.so (argument marshalling only).
+
+Every call checks tensor dtypes/devices/shapes, allocates missing outputs with
+torch on the input's device, and forwards raw device pointers plus the current
+torch stream to the C-ABI. All arithmetic happens in the HIP kernels; if the
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbga.so")
+
+STATUS_NAMES = {0: "BGA_OK", 1: "BGA_ERR_NULL", 2: "BGA_ERR_SHAPE", 3: "BGA_ERR_UNSUPPORTED",
+                4: "BGA_ERR_ALIGN", 5: "BGA_ERR_WORKSPACE", 6: "BGA_ERR_ALIAS", 7: "BGA_ERR_HIP"}
+
+# Every symbol declared in include/bga.h.
+EXPORTS = ("bga_packed_gqa_prefill", "bga_shared_prefix_decode", "bga_suffix_reorder",
+           "bga_beam_topk_workspace_size", "bga_beam_topk", "bga_status_string", "bga_last_hip_error",
+           "bga_version")
+
+
+class BgaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {detail or STATUS_NAMES.get(status, status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_bga_packed_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.bga_packed_gqa_prefill.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, P, P, P]
+    L.bga_shared_prefix_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P, P]
+    L.bga_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, P]
+    L.bga_beam_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.bga_beam_topk_workspace_size.restype = sz
+    L.bga_beam_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
+    L.bga_status_string.argtypes = [i32]
+    L.bga_status_string.restype = ctypes.c_char_p
+    L.bga_last_hip_error.argtypes = []
+    L.bga_version.argtypes = []
+    for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_suffix_reorder, L.bga_beam_topk,
+              L.bga_last_hip_error, L.bga_version):
+        f.restype = i32
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = lib.bga_status_string(status).decode()
+        if status == 7:
+            detail += f" (hipError {lib.bga_last_hip_error()})"
+        raise BgaError(status, where, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_gqa_prefill(q, k, v, cu_seqlens, max_seqlen: int, softmax_scale=None, out=None, lse=None,
+                       want_lse: bool = True):
+    """Packed causal GQA prefill. q [T,Nq,D], k/v [T,Nkv,D] bf16; cu_seqlens int32 [B+1] on the GPU.
+    Returns (out [T,Nq,D] bf16, lse [T,Nq] fp32 or None)."""
+    _need(q, "q", torch.bfloat16, ndim=3)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, dev, 3)
+    _need(v, "v", torch.bfloat16, dev, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+    t, nq, d = q.shape
+    nkv = k.shape[1]
+    if k.shape != (t, nkv, d) or v.shape != k.shape:
+        raise ValueError("k/v must be [T, Nkv, D] matching q")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((t, nq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    st = lib.bga_packed_gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, t,
+                                    int(max_seqlen), nq, nkv, d, float(softmax_scale), _ptr(out), _ptr(lse),
+                                    _stream(q))
+    _check(st, "bga_packed_gqa_prefill")
+    return out, lse
+
+
+def shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, suffix_len: int, softmax_scale=None,
+                         out=None, lse=None, want_lse: bool = True):
+    """Shared-prefix beam decode. q [R,W,Nq,D]; prefix [R,Lp,Nkv,D]; suffix [R,W,Ls_cap,Nkv,D] (bf16).
+    Returns (out [R,W,Nq,D] bf16, lse [R,W,Nq] fp32 or None)."""
+    _need(q, "q", torch.bfloat16, ndim=4)
+    dev = q.device
+    _need(prefix_k, "prefix_k", torch.bfloat16, dev, 4)
+    _need(prefix_v, "prefix_v", torch.bfloat16, dev, 4)
+    _need(suffix_k, "suffix_k", torch.bfloat16, dev, 5)
+    _need(suffix_v, "suffix_v", torch.bfloat16, dev, 5)
+    r, w, nq, d = q.shape
+    lp, nkv = prefix_k.shape[1], prefix_k.shape[2]
+    ls_cap = suffix_k.shape[2]
+    if prefix_k.shape != (r, lp, nkv, d) or prefix_v.shape != prefix_k.shape:
+        raise ValueError("prefix K/V must be [R, Lp, Nkv, D]")
+    if suffix_k.shape != (r, w, ls_cap, nkv, d) or suffix_v.shape != suffix_k.shape:
+        raise ValueError("suffix K/V must be [R, W, Ls_cap, Nkv, D]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((r, w, nq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    st = lib.bga_shared_prefix_decode(_ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k), _ptr(suffix_v), r, w,
+                                      lp, int(suffix_len), ls_cap, nq, nkv, d, float(softmax_scale), _ptr(out),
+                                      _ptr(lse), _stream(q))
+    _check(st, "bga_shared_prefix_decode")
+    return out, lse
+
+
+def suffix_reorder(src_k, src_v, parent, suffix_len: int, dst_k=None, dst_v=None, src_tokens=None,
+                   dst_tokens=None, num_tokens: int = 0):
+    """Gather suffix K/V (and optionally token history) by parent index, out of place.
+    src/dst [R,W,Ls_cap,Nkv,D] bf16; parent [R,W] int32; tokens [R,W,tok_cap] int32."""
+    _need(src_k, "src_k", torch.bfloat16, ndim=5)
+    dev = src_k.device
+    _need(src_v, "src_v", torch.bfloat16, dev, 5)
+    _need(parent, "parent", torch.int32, dev, 2)
+    r, w, ls_cap, nkv, d = src_k.shape
+    if dst_k is None:
+        dst_k = torch.empty_like(src_k)
+    if dst_v is None:
+        dst_v = torch.empty_like(src_v)
+    _need(dst_k, "dst_k", torch.bfloat16, dev, 5)
+    _need(dst_v, "dst_v", torch.bfloat16, dev, 5)
+    tok_cap = 0
+    if src_tokens is not None:
+        _need(src_tokens, "src_tokens", torch.int32, dev, 3)
+        tok_cap = src_tokens.shape[2]
+        if dst_tokens is None:
+            dst_tokens = torch.empty_like(src_tokens)
+        _need(dst_tokens, "dst_tokens", torch.int32, dev, 3)
+    st = lib.bga_suffix_reorder(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(parent), _ptr(src_tokens),
+                                _ptr(dst_tokens), r, w, int(suffix_len), ls_cap, nkv, d, int(num_tokens), tok_cap,
+                                _stream(src_k))
+    _check(st, "bga_suffix_reorder")
+    return (dst_k, dst_v) if src_tokens is None else (dst_k, dst_v, dst_tokens)
+
+
+def beam_topk_workspace_size(num_requests, num_src_beams, vocab, k_local, k_global) -> int:
+    return int(lib.bga_beam_topk_workspace_size(num_requests, num_src_beams, vocab, k_local, k_global))
+
+
+def beam_topk(logits, cum_scores, k_local: int, k_global: int, workspace=None, want_local: bool = False,
+              want_lse: bool = False, out=None):
+    """Two-stage beam candidate selection. logits [R,W_in,V] bf16; cum_scores [R,W_in] fp32 or None.
+    Returns dict(tokens, parents, scores[, local_tokens, local_scores][, row_lse])."""
+    _need(logits, "logits", torch.bfloat16, ndim=3)
+    dev = logits.device
+    r, w_in, vocab = logits.shape
+    if cum_scores is not None:
+        _need(cum_scores, "cum_scores", torch.float32, dev, 2)
+    need = beam_topk_workspace_size(r, w_in, vocab, k_local, k_global)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    res = out if out is not None else {}
+    res.setdefault("tokens", torch.empty((r, k_global), dtype=torch.int32, device=dev))
+    res.setdefault("parents", torch.empty((r, k_global), dtype=torch.int32, device=dev))
+    res.setdefault("scores", torch.empty((r, k_global), dtype=torch.float32, device=dev))
+    if want_local:
+        res.setdefault("local_tokens", torch.empty((r, w_in, k_local), dtype=torch.int32, device=dev))
+        res.setdefault("local_scores", torch.empty((r, w_in, k_local), dtype=torch.float32, device=dev))
+    if want_lse:
+        res.setdefault("row_lse", torch.empty((r, w_in), dtype=torch.float32, device=dev))
+    st = lib.bga_beam_topk(_ptr(logits), _ptr(cum_scores), r, w_in, vocab, int(k_local), int(k_global),
+                           _ptr(res["tokens"]), _ptr(res["parents"]), _ptr(res["scores"]),
+                           _ptr(res.get("local_tokens")), _ptr(res.get("local_scores")), _ptr(res.get("row_lse")),
+                           _ptr(workspace), workspace.numel(), _stream(logits))
+    _check(st, "bga_beam_topk")
+    return res

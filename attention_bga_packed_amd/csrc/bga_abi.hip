@@ -1,0 +1,194 @@
+// C-ABI entry points of libbga: host-side argument validation, then one or two
+// kernel launches on the caller's stream. Nothing is enqueued when validation
+// fails. See include/bga.h for the contract of every call.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/bga.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bga_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return BGA_OK;
+    g_last_hip_error = (int32_t)e;
+    return BGA_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool heads_ok(int32_t nq, int32_t nkv)
+{
+    return nq > 0 && nkv > 0 && nq % nkv == 0 && nq / nkv <= BGA_MAX_GROUP;
+}
+
+// [a, a + na) and [b, b + nb) overlap (bytes)
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bga_bf16 *v,
+                                  const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                  int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
+                                  hipStream_t stream)
+{
+    if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0) return BGA_ERR_SHAPE;
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return BGA_ERR_SHAPE;
+    if (!heads_ok(num_q_heads, num_kv_heads)) return BGA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || max_seqlen > BGA_MAX_SEQLEN) return BGA_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
+    if (!cu_seqlens) return BGA_ERR_NULL;
+    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return BGA_OK;
+    if (!q || !k || !v || !out) return BGA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(cu_seqlens, 4) ||
+        (lse && !aligned(lse, 4)))
+        return BGA_ERR_ALIGN;
+    const size_t qbytes = (size_t)total_tokens * num_q_heads * head_dim * 2;
+    const size_t kvbytes = (size_t)total_tokens * num_kv_heads * head_dim * 2;
+    if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kvbytes) || overlap(out, qbytes, v, kvbytes))
+        return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_packed_prefill(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_q_heads,
+                                                 num_kv_heads, head_dim, softmax_scale, out, lse, stream));
+}
+
+bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k, const bga_bf16 *prefix_v,
+                                    const bga_bf16 *suffix_k, const bga_bf16 *suffix_v, int32_t num_requests,
+                                    int32_t beam_width, int32_t prefix_len, int32_t suffix_len,
+                                    int32_t suffix_cap, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
+                                    hipStream_t stream)
+{
+    if (num_requests < 0 || beam_width < 0 || prefix_len < 0 || suffix_len < 0 || suffix_cap < 0)
+        return BGA_ERR_SHAPE;
+    if (suffix_len > suffix_cap || prefix_len + suffix_len < 1) return BGA_ERR_SHAPE;
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return BGA_ERR_SHAPE;
+    if (!heads_ok(num_q_heads, num_kv_heads)) return BGA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
+    if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX || prefix_len > BGA_MAX_SEQLEN)
+        return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * num_kv_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
+    if (num_requests == 0 || beam_width == 0) return BGA_OK;
+    if (!q || !out) return BGA_ERR_NULL;
+    if (prefix_len > 0 && (!prefix_k || !prefix_v)) return BGA_ERR_NULL;
+    if (suffix_len > 0 && (!suffix_k || !suffix_v)) return BGA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(prefix_k, 16) || !aligned(prefix_v, 16) ||
+        !aligned(suffix_k, 16) || !aligned(suffix_v, 16) || (lse && !aligned(lse, 4)))
+        return BGA_ERR_ALIGN;
+    const size_t obytes = (size_t)num_requests * beam_width * num_q_heads * head_dim * 2;
+    const size_t pbytes = (size_t)num_requests * prefix_len * num_kv_heads * head_dim * 2;
+    const size_t sbytes = (size_t)num_requests * beam_width * suffix_cap * num_kv_heads * head_dim * 2;
+    if (overlap(out, obytes, q, obytes) || overlap(out, obytes, prefix_k, pbytes) ||
+        overlap(out, obytes, prefix_v, pbytes) || overlap(out, obytes, suffix_k, sbytes) ||
+        overlap(out, obytes, suffix_v, sbytes))
+        return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, num_requests,
+                                                       beam_width, prefix_len, suffix_len, suffix_cap,
+                                                       num_q_heads, num_kv_heads, head_dim, softmax_scale, out,
+                                                       lse, stream));
+}
+
+bga_status bga_suffix_reorder(const bga_bf16 *src_k, const bga_bf16 *src_v, bga_bf16 *dst_k, bga_bf16 *dst_v,
+                              const int32_t *parent, const int32_t *src_tokens, int32_t *dst_tokens,
+                              int32_t num_requests, int32_t beam_width, int32_t suffix_len, int32_t suffix_cap,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t num_tokens, int32_t tok_cap,
+                              hipStream_t stream)
+{
+    if (num_requests < 0 || beam_width < 0 || suffix_len < 0 || suffix_cap < 0 || suffix_len > suffix_cap)
+        return BGA_ERR_SHAPE;
+    if (num_kv_heads <= 0) return BGA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
+    if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX) return BGA_ERR_UNSUPPORTED;
+    if ((src_tokens == nullptr) != (dst_tokens == nullptr)) return BGA_ERR_NULL;
+    if (src_tokens && (num_tokens < 0 || tok_cap < 0 || num_tokens > tok_cap)) return BGA_ERR_SHAPE;
+    if (num_requests == 0 || beam_width == 0) return BGA_OK;
+    if (!parent || !src_k || !src_v || !dst_k || !dst_v) return BGA_ERR_NULL;
+    if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) ||
+        !aligned(parent, 4) || (src_tokens && (!aligned(src_tokens, 4) || !aligned(dst_tokens, 4))))
+        return BGA_ERR_ALIGN;
+    const size_t kv = (size_t)num_requests * beam_width * suffix_cap * num_kv_heads * head_dim * 2;
+    if (overlap(dst_k, kv, src_k, kv) || overlap(dst_k, kv, src_v, kv) || overlap(dst_v, kv, src_k, kv) ||
+        overlap(dst_v, kv, src_v, kv) || overlap(dst_k, kv, dst_v, kv))
+        return BGA_ERR_ALIAS;
+    if (src_tokens) {
+        const size_t tb = (size_t)num_requests * beam_width * tok_cap * 4;
+        if (overlap(dst_tokens, tb, src_tokens, tb)) return BGA_ERR_ALIAS;
+    }
+    return hip_status(bga::launch_suffix_reorder(src_k, src_v, dst_k, dst_v, parent, src_tokens, dst_tokens,
+                                                 num_requests, beam_width, suffix_len, suffix_cap, num_kv_heads,
+                                                 head_dim, src_tokens ? num_tokens : 0, tok_cap, stream));
+}
+
+static bool topk_sizes_ok(int32_t R, int32_t W_in, int32_t V, int32_t k_local, int32_t k_global)
+{
+    if (R < 0 || W_in <= 0 || V <= 0 || k_local <= 0 || k_global <= 0) return false;
+    if (W_in > BGA_MAX_BEAMS || V > BGA_MAX_VOCAB || k_local > V || k_local > BGA_MAX_K || k_global > BGA_MAX_K)
+        return false;
+    if ((int64_t)k_global > (int64_t)W_in * k_local) return false;
+    return true;
+}
+
+size_t bga_beam_topk_workspace_size(int32_t num_requests, int32_t num_src_beams, int32_t vocab, int32_t k_local,
+                                    int32_t k_global)
+{
+    if (!topk_sizes_ok(num_requests, num_src_beams, vocab, k_local, k_global)) return 0;
+    return bga::topk_workspace_layout(num_requests, num_src_beams, k_local).total;
+}
+
+bga_status bga_beam_topk(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
+                         int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
+                         int32_t *out_tokens, int32_t *out_parents, float *out_scores, int32_t *local_tokens,
+                         float *local_scores, float *row_lse, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    if (num_requests < 0 || num_src_beams <= 0 || vocab <= 0 || k_local <= 0 || k_global <= 0)
+        return BGA_ERR_SHAPE;
+    if ((int64_t)k_global > (int64_t)num_src_beams * k_local || k_local > vocab) return BGA_ERR_SHAPE;
+    if (!topk_sizes_ok(num_requests, num_src_beams, vocab, k_local, k_global)) return BGA_ERR_UNSUPPORTED;
+    if (num_requests == 0) return BGA_OK;
+    if (!logits || !out_tokens || !out_parents || !out_scores) return BGA_ERR_NULL;
+    const size_t need = bga::topk_workspace_layout(num_requests, num_src_beams, k_local).total;
+    if (!workspace || workspace_bytes < need) return BGA_ERR_WORKSPACE;
+    if (!aligned(logits, 16) || !aligned(workspace, 16) || !aligned(out_tokens, 4) || !aligned(out_parents, 4) ||
+        !aligned(out_scores, 4) || (cum_scores && !aligned(cum_scores, 4)) ||
+        (local_tokens && !aligned(local_tokens, 4)) || (local_scores && !aligned(local_scores, 4)) ||
+        (row_lse && !aligned(row_lse, 4)))
+        return BGA_ERR_ALIGN;
+    const size_t lbytes = (size_t)num_requests * num_src_beams * vocab * 2;
+    if (overlap(workspace, need, logits, lbytes)) return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_beam_topk(logits, cum_scores, num_requests, num_src_beams, vocab, k_local,
+                                            k_global, out_tokens, out_parents, out_scores, local_tokens,
+                                            local_scores, row_lse, workspace, stream));
+}
+
+const char *bga_status_string(bga_status s)
+{
+    switch (s) {
+    case BGA_OK: return "BGA_OK";
+    case BGA_ERR_NULL: return "BGA_ERR_NULL: a required pointer is NULL";
+    case BGA_ERR_SHAPE: return "BGA_ERR_SHAPE: inconsistent or negative sizes";
+    case BGA_ERR_UNSUPPORTED: return "BGA_ERR_UNSUPPORTED: head_dim, group size or a cap is not supported";
+    case BGA_ERR_ALIGN: return "BGA_ERR_ALIGN: a pointer is not aligned as required";
+    case BGA_ERR_WORKSPACE: return "BGA_ERR_WORKSPACE: workspace missing or too small";
+    case BGA_ERR_ALIAS: return "BGA_ERR_ALIAS: an output overlaps an input";
+    case BGA_ERR_HIP: return "BGA_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown bga_status";
+}
+
+int32_t bga_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t bga_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Shared-prefix beam decode attention for gfx950.
+//
+// Article section 3.2 ("请求内共享前缀的 K/V 布局"): one prompt K/V per request
+// [L_p, Nkv, D], a short suffix K/V per beam [W, L_s, Nkv, D], one query token
+// per beam [W, Nq, D], and O_b = Attention(Q_b, [prefix_K; suffix_K[b]],
+// [prefix_V; suffix_V[b]]) computed in a single fp32 online-softmax state
+// without any concatenated tensor.
+//
+// The prefix segment is the dense part: for a (request, kv head) all W beams'
+// G query heads form a [W*G, D] block that multiplies the same [L_p, D] prefix,
+// so it runs on MFMA exactly like a prefill tile (no mask except the ragged end
+// of the prefix). A workgroup takes 128 of those query rows (4 waves x 32) and
+// streams the prefix through LDS once; the prefix is therefore read from HBM
+// once per (request, kv head) and from L2 by the other row blocks. The suffix
+// segment is a handful of per-beam keys: each lane pair (lanes l and l^32, one
+// query row) forms the dot products with its own beam's suffix keys from the
+// d-halves it already holds and folds them into the same (m, l, O) state.
+//
+// Grid = (R*Nkv, row blocks). Consecutive workgroups are dealt round-robin over
+// the 8 XCDs, so with R*Nkv a multiple of 8 every row block of one
+// (request, kv head) lands on the same XCD and shares its L2 copy of the prefix.
+#include "attn_tile.hpp"
+#include "internal.hpp"
+
+namespace bga {
+
+template <int D>
+__global__ __launch_bounds__(256) void shared_prefix_decode_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ pk, const uint16_t *__restrict__ pv,
+    const uint16_t *__restrict__ sk, const uint16_t *__restrict__ sv, int W, int Lp, int Ls, int Ls_cap, int nq,
+    int nkv, int group, float scale, uint16_t *__restrict__ out, float *__restrict__ lse)
+{
+    using T = AttnTile<D>;
+    extern __shared__ __align__(16) uint16_t smem[];
+
+    const int rg = blockIdx.x;
+    const int r = rg / nkv, g = rg % nkv;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int rows = W * group;
+    const int n = blockIdx.y * 128 + w * 32 + col;  // query row within (r, g): beam * G + head-in-group
+    const bool row_valid = n < rows;
+    const int beam = row_valid ? n / group : 0;
+    const int head = g * group + (row_valid ? n % group : 0);
+    const bool wave_active = blockIdx.y * 128 + w * 32 < rows;
+    const size_t qrow_idx = ((size_t)r * W + beam) * nq + head;
+
+    bf16x8 qop[D / 16];
+    load_q_operand<D>(qop, q + qrow_idx * D, row_valid);
+
+    WaveAttn<D> st;
+    st.init();
+    const float c2 = scale * kLog2e;
+
+    // ---- prefix segment: MFMA tiles through LDS, shared by the 4 waves
+    const size_t row_stride = (size_t)nkv * D;
+    const uint16_t *kbase = pk + (size_t)r * Lp * row_stride + (size_t)g * D;
+    const uint16_t *vbase = pv + (size_t)r * Lp * row_stride + (size_t)g * D;
+    const int nkt = (Lp + T::BN - 1) / T::BN;
+    T tl;
+    if (nkt > 0) {
+        tl.load(kbase, vbase, row_stride, 0, Lp, tid, nthr);
+        tl.store(smem, tid, nthr);
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int kstart = kt * T::BN;
+        if (kt + 1 < nkt) tl.load(kbase, vbase, row_stride, kstart + T::BN, Lp, tid, nthr);
+        __syncthreads();
+        if (wave_active) {
+            const uint16_t *Ks = smem + (kt & 1) * T::STAGE;
+            st.tile(Ks, Ks + T::K_ELEMS, qop, c2, kstart + T::BN > Lp, kstart, Lp - 1);
+        }
+        if (kt + 1 < nkt) tl.store(smem + ((kt + 1) & 1) * T::STAGE, tid, nthr);
+    }
+    if (!wave_active) return;
+
+    // ---- suffix segment: this beam's own keys, folded into the same state
+    const size_t sbase = (((size_t)r * W + beam) * Ls_cap * nkv + g) * D;
+    for (int j = 0; j < Ls; ++j) {
+        const uint16_t *krow = sk + sbase + (size_t)j * row_stride;
+        const uint16_t *vrow = sv + sbase + (size_t)j * row_stride;
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 kv = {0u, 0u, 0u, 0u};
+            if (row_valid) kv = *(const u32x4 *)(krow + ks * 16 + half * 8);
+            const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(kv[e]), part);
+                part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(kv[e]), part);
+            }
+        }
+        const float s = part + xor32(part);
+        const float m_new = fmaxf(st.m, s);
+        const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);
+        const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
+        st.l = st.l * alpha + (half == 0 ? p : 0.f);
+        st.m = m_new;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int rgi = 0; rgi < 4; ++rgi) {
+                u32x2 vv = {0u, 0u};
+                if (row_valid) vv = *(const u32x2 *)(vrow + b * 32 + rgi * 8 + half * 4);
+                st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
+                st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
+                st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
+                st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
+            }
+    }
+    st.finish(out + qrow_idx * D, lse ? lse + qrow_idx : nullptr, row_valid, scale);
+}
+
+template <int D>
+static hipError_t launch_decode_d(const uint16_t *q, const uint16_t *pk, const uint16_t *pv, const uint16_t *sk,
+                                  const uint16_t *sv, int R, int W, int Lp, int Ls, int Ls_cap, int nq, int nkv,
+                                  float scale, uint16_t *out, float *lse, hipStream_t stream)
+{
+    const int group = nq / nkv;
+    const int rows = W * group;
+    const size_t smem = AttnTile<D>::SMEM_BYTES;
+    hipError_t e = hipFuncSetAttribute((const void *)shared_prefix_decode_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    dim3 grid(R * nkv, (rows + 127) / 128), block(256);
+    hipLaunchKernelGGL(shared_prefix_decode_kernel<D>, grid, block, smem, stream, q, pk, pv, sk, sv, W, Lp, Ls,
+                       Ls_cap, nq, nkv, group, scale, out, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_prefix_decode(const uint16_t *q, const uint16_t *pk, const uint16_t *pv,
+                                       const uint16_t *sk, const uint16_t *sv, int R, int W, int Lp, int Ls,
+                                       int Ls_cap, int nq, int nkv, int d, float scale, uint16_t *out, float *lse,
+                                       hipStream_t stream)
+{
+    if (d == 64)
+        return launch_decode_d<64>(q, pk, pv, sk, sv, R, W, Lp, Ls, Ls_cap, nq, nkv, scale, out, lse, stream);
+    return launch_decode_d<128>(q, pk, pv, sk, sv, R, W, Lp, Ls, Ls_cap, nq, nkv, scale, out, lse, stream);
+}
+
+}  // namespace bga

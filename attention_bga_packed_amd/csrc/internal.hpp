@@ -1,0 +1,39 @@
+// Host-side launchers of libbga's kernels. Arguments are validated by the
+// C-ABI layer (bga_abi.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bga {
+
+// Every launcher returns hipSuccess or the launch error.
+
+hipError_t launch_packed_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu,
+                                 int num_seqs, int max_seqlen, int nq, int nkv, int d, float scale, uint16_t *out,
+                                 float *lse, hipStream_t stream);
+
+hipError_t launch_shared_prefix_decode(const uint16_t *q, const uint16_t *pk, const uint16_t *pv,
+                                       const uint16_t *sk, const uint16_t *sv, int R, int W, int Lp, int Ls,
+                                       int Ls_cap, int nq, int nkv, int d, float scale, uint16_t *out, float *lse,
+                                       hipStream_t stream);
+
+hipError_t launch_suffix_reorder(const uint16_t *src_k, const uint16_t *src_v, uint16_t *dst_k, uint16_t *dst_v,
+                                 const int32_t *parent, const int32_t *src_tok, int32_t *dst_tok, int R, int W,
+                                 int Ls, int Ls_cap, int nkv, int d, int ntok, int tok_cap, hipStream_t stream);
+
+// Workspace layout of the beam top-K (offsets in bytes, 256-byte aligned parts).
+struct TopkWorkspace {
+    size_t local_tok;    // int32 [R, W_in, k_local]
+    size_t local_score;  // float [R, W_in, k_local]
+    size_t total;
+};
+TopkWorkspace topk_workspace_layout(int R, int W_in, int k_local);
+
+hipError_t launch_beam_topk(const uint16_t *logits, const float *cum, int R, int W_in, int V, int k_local,
+                            int k_global, int32_t *out_tok, int32_t *out_par, float *out_score,
+                            int32_t *local_tok, float *local_score, float *row_lse, void *workspace,
+                            hipStream_t stream);
+
+}  // namespace bga

@@ -1,0 +1,184 @@
+/*
+ * libbga — the attention hot path of a bounded-generation SLM inference engine,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Meituan engineering article
+ * "SLM 生成式高并发推理引擎：延迟约束下的有效吞吐优化":
+ *   - packed variable-length causal GQA prefill       (section 3.1)
+ *   - shared-prefix beam-search decode attention      (section 3.2)
+ *   - parent-index suffix K/V and token reorder        (sections 3.2, 3.3)
+ *   - two-stage beam candidate selection              (section 3.3)
+ *
+ * Conventions for every entry point
+ *   - All tensors are row-major and contiguous, head_dim fastest.
+ *   - bf16 tensors are passed as raw 16-bit patterns (bga_bf16).
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise. The
+ *     caller owns all memory; the library allocates nothing, keeps no state
+ *     between calls, never synchronizes, and only enqueues work on `stream`.
+ *   - Outputs are fully overwritten within their declared extents; nothing
+ *     outside them is written.
+ *   - Problems that can be checked on the host (null pointers, sizes, caps,
+ *     alignment, workspace size, overlapping buffers) return a nonzero status
+ *     BEFORE any device call: nothing is enqueued. BGA_ERR_HIP reports a failed
+ *     launch; bga_last_hip_error() then returns the hipError_t.
+ *   - Preconditions on device data (valid cu_seqlens, parent indices in range,
+ *     finite logits) are documented per call and not checked.
+ *   - Calls on different streams may run concurrently; the library is reentrant.
+ */
+#ifndef BGA_H
+#define BGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t bga_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+    BGA_OK = 0,
+    BGA_ERR_NULL = 1,        /* a required pointer is NULL */
+    BGA_ERR_SHAPE = 2,       /* inconsistent or negative sizes */
+    BGA_ERR_UNSUPPORTED = 3, /* head_dim, group size, or a cap not supported */
+    BGA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+    BGA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    BGA_ERR_ALIAS = 6,       /* output overlaps an input that must stay intact */
+    BGA_ERR_HIP = 7          /* a HIP launch failed; see bga_last_hip_error() */
+} bga_status;
+
+/* Caps (the article bounds its workloads to <= 400 beams, <= 5 generated
+ * tokens and prompts averaging under 500 tokens, section 1.2). */
+#define BGA_MAX_GROUP 16        /* num_q_heads / num_kv_heads */
+#define BGA_MAX_SEQLEN 65536    /* longest packed sequence */
+#define BGA_MAX_BEAMS 1024      /* beam_width / num_src_beams */
+#define BGA_MAX_SUFFIX 64       /* suffix_cap */
+#define BGA_MAX_K 1024          /* k_local and k_global */
+#define BGA_MAX_VOCAB 163840    /* vocabulary size */
+
+/*
+ * Packed variable-length causal GQA prefill (article section 3.1: the packed
+ * Q/K/V/O layout, the block-diagonal causal mask implied by the sequence
+ * boundary, and the blocked K/V scan with an fp32 online-softmax state).
+ *
+ *   q        [T, num_q_heads,  head_dim]  bf16
+ *   k, v     [T, num_kv_heads, head_dim]  bf16
+ *   cu_seqlens [num_seqs + 1] int32: cu[0] = 0, non-decreasing, cu[num_seqs] =
+ *            total_tokens = T. Sequence i owns rows cu[i] .. cu[i+1]-1. Zero-length
+ *            sequences are allowed.
+ *   max_seqlen >= every cu[i+1]-cu[i] (precondition; rows of a longer sequence
+ *            beyond max_seqlen are not written).
+ *   Query head h reads K/V head h / (num_q_heads / num_kv_heads).
+ *   A query at position t of its sequence attends to positions 0..t of the
+ *   same sequence; scores are softmax_scale * <q, k>.
+ *   out      [T, num_q_heads, head_dim] bf16 (round to nearest even)
+ *   lse      [T, num_q_heads] fp32, natural-log log-sum-exp of the scaled
+ *            scores, or NULL.
+ * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with group
+ * <= BGA_MAX_GROUP; num_seqs <= 65535. q, k, v, out 16-byte aligned; lse and
+ * cu_seqlens 4-byte aligned.
+ */
+bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bga_bf16 *v,
+                                  const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                  int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
+                                  hipStream_t stream);
+
+/*
+ * Shared-prefix beam decode attention (article section 3.2: one prompt K/V per
+ * request, a short suffix K/V per beam, and
+ *   O_b = Attention(Q_b, [prefix_K; suffix_K[b]], [prefix_V; suffix_V[b]])
+ * evaluated in one fp32 online-softmax state without building the
+ * concatenation).
+ *
+ *   q          [R, W, num_q_heads, head_dim] bf16 (one query token per beam)
+ *   prefix_k/v [R, prefix_len, num_kv_heads, head_dim] bf16
+ *   suffix_k/v [R, W, suffix_cap, num_kv_heads, head_dim] bf16; positions
+ *              0 .. suffix_len-1 are read (suffix_len counts the current token).
+ *   No mask: every prefix and suffix key precedes the query.
+ *   out        [R, W, num_q_heads, head_dim] bf16
+ *   lse        [R, W, num_q_heads] fp32 natural-log log-sum-exp, or NULL
+ * Requires prefix_len + suffix_len >= 1, 0 <= suffix_len <= suffix_cap <=
+ * BGA_MAX_SUFFIX, W <= BGA_MAX_BEAMS, head_dim in {64, 128}, group <=
+ * BGA_MAX_GROUP; suffix pointers may be NULL only when suffix_len == 0.
+ * q, prefix, suffix and out 16-byte aligned; lse 4-byte aligned.
+ */
+bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k, const bga_bf16 *prefix_v,
+                                    const bga_bf16 *suffix_k, const bga_bf16 *suffix_v, int32_t num_requests,
+                                    int32_t beam_width, int32_t prefix_len, int32_t suffix_len,
+                                    int32_t suffix_cap, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
+                                    hipStream_t stream);
+
+/*
+ * Parent-index reorder (article sections 3.2 and 3.3: after candidate
+ * selection only the retained beams' short suffix K/V, token history and
+ * scores move; the prompt K/V never does).
+ *
+ *   src_k/src_v, dst_k/dst_v [R, W, suffix_cap, num_kv_heads, head_dim] bf16
+ *   parent     [R, W] int32; new beam b of request r copies beam parent[r, b]
+ *              (precondition 0 <= parent < W; an out-of-range parent yields
+ *              zeros for that beam).
+ *   Positions 0 .. suffix_len-1 are copied; positions >= suffix_len of dst are
+ *   left untouched.
+ *   src_tokens/dst_tokens [R, W, tok_cap] int32, optional (both NULL or both
+ *   set): the first num_tokens entries of each beam are copied the same way.
+ * Out of place: dst buffers must not overlap src buffers (BGA_ERR_ALIAS).
+ * K/V pointers 16-byte aligned.
+ */
+bga_status bga_suffix_reorder(const bga_bf16 *src_k, const bga_bf16 *src_v, bga_bf16 *dst_k, bga_bf16 *dst_v,
+                              const int32_t *parent, const int32_t *src_tokens, int32_t *dst_tokens,
+                              int32_t num_requests, int32_t beam_width, int32_t suffix_len, int32_t suffix_cap,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t num_tokens, int32_t tok_cap,
+                              hipStream_t stream);
+
+/* Bytes of device workspace bga_beam_topk needs for these sizes (0 on bad sizes). */
+size_t bga_beam_topk_workspace_size(int32_t num_requests, int32_t num_src_beams, int32_t vocab,
+                                    int32_t k_local, int32_t k_global);
+
+/*
+ * Two-stage beam candidate selection (article section 3.3):
+ *  stage 1, per source beam row (r, b): the k_local token ids with the largest
+ *    bf16 logits (equal logits: lower id first; -0 equals +0), ranked;
+ *    lse = fp32 log-sum-exp of the row over the full vocabulary (float
+ *    logits); lp = x - lse and score = cum[r, b] + lp, each one fp32 operation.
+ *  stage 2, per request: the W_in * k_local candidates flattened as
+ *    f = b * k_local + j; the k_global best scores (equal scores: lower f
+ *    first), sorted best first; parent = f / k_local; token = the stage-1 id at
+ *    (parent, f % k_local); out score = that candidate's score (the new
+ *    cumulative score).
+ *
+ *   logits     [R, W_in, vocab] bf16, finite (precondition)
+ *   cum_scores [R, W_in] fp32, or NULL for all zero (first step)
+ *   out_tokens, out_parents [R, k_global] int32; out_scores [R, k_global] fp32
+ *   local_tokens [R, W_in, k_local] int32 and local_scores fp32: optional
+ *   row_lse    [R, W_in] fp32: optional
+ *   workspace  device memory of >= bga_beam_topk_workspace_size(...) bytes,
+ *              16-byte aligned; its contents on entry do not matter.
+ * Requires 1 <= k_local <= min(vocab, BGA_MAX_K), 1 <= k_global <=
+ * min(W_in * k_local, BGA_MAX_K), W_in <= BGA_MAX_BEAMS, vocab <= BGA_MAX_VOCAB.
+ * logits 16-byte aligned; vocab % 8 == 0 is the fast path.
+ */
+bga_status bga_beam_topk(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
+                         int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
+                         int32_t *out_tokens, int32_t *out_parents, float *out_scores, int32_t *local_tokens,
+                         float *local_scores, float *row_lse, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *bga_status_string(bga_status s);
+
+/* hipError_t of the most recent BGA_ERR_HIP on the calling thread (0 if none). */
+int32_t bga_last_hip_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t bga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BGA_H */

@@ -1,0 +1,117 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every symbol
+include/bga.h declares, and rejects bad arguments with the documented status
+before making any device call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import attention_bga_packed_amd as mod
+    return mod
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "bga.h")).read()
+    return sorted(set(re.findall(r"\b(bga_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header(m):
+    syms = header_symbols()
+    assert syms == sorted(m.EXPORTS)
+    raw = ctypes.CDLL(m.LIB_PATH)
+    for s in syms:
+        assert hasattr(raw, s), s
+
+
+def test_status_strings(m):
+    for code in range(8):
+        s = m.lib.bga_status_string(code).decode()
+        assert s.startswith("BGA_")
+    assert m.lib.bga_last_hip_error() == 0
+    assert m.lib.bga_version() >= 100
+
+
+P = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced on these paths
+
+
+def prefill(m, q=P, k=2 * P, v=3 * P, cu=4 * P, B=3, T=62, maxL=40, nq=4, nkv=2, d=64, scale=0.125,
+            out=5 * P, lse=6 * P):
+    return m.lib.bga_packed_gqa_prefill(q, k, v, cu, B, T, maxL, nq, nkv, d, scale, out, lse, None)
+
+
+def test_prefill_errors(m):
+    assert prefill(m, nq=5, nkv=2) == 2
+    assert prefill(m, d=96) == 3
+    assert prefill(m, nq=34, nkv=2) == 3          # group 17
+    assert prefill(m, T=-1) == 2
+    assert prefill(m, scale=0.0) == 2
+    assert prefill(m, cu=None) == 1
+    assert prefill(m, q=None) == 1
+    assert prefill(m, out=None) == 1
+    assert prefill(m, k=2 * P + 8) == 4
+    assert prefill(m, lse=6 * P + 2) == 4
+    assert prefill(m, out=P) == 6                 # out aliases q
+    assert prefill(m, maxL=1 << 20) == 3
+    assert prefill(m, T=0) == 0                   # nothing to do, nothing launched
+    assert prefill(m, B=0) == 0
+
+
+def decode(m, q=P, pk=2 * P, pv=3 * P, sk=4 * P, sv=5 * P, R=2, W=4, Lp=8, Ls=2, cap=3, nq=4, nkv=2, d=64,
+           scale=0.125, out=6 * P, lse=7 * P):
+    return m.lib.bga_shared_prefix_decode(q, pk, pv, sk, sv, R, W, Lp, Ls, cap, nq, nkv, d, scale, out, lse, None)
+
+
+def test_decode_errors(m):
+    assert decode(m, Ls=4, cap=3) == 2
+    assert decode(m, Lp=0, Ls=0) == 2
+    assert decode(m, W=2000) == 3
+    assert decode(m, cap=100, Ls=1) == 3
+    assert decode(m, d=80) == 3
+    assert decode(m, sk=None) == 1
+    assert decode(m, pk=None) == 1
+    assert decode(m, q=P + 4) == 4
+    assert decode(m, out=P) == 6
+    assert decode(m, R=0) == 0
+
+
+def reorder(m, sk=P, sv=2 * P, dk=3 * P, dv=4 * P, par=5 * P, st=None, dt=None, R=2, W=4, Ls=2, cap=3, nkv=2,
+            d=64, nt=0, tc=0):
+    return m.lib.bga_suffix_reorder(sk, sv, dk, dv, par, st, dt, R, W, Ls, cap, nkv, d, nt, tc, None)
+
+
+def test_reorder_errors(m):
+    assert reorder(m, Ls=4) == 2
+    assert reorder(m, st=6 * P) == 1              # tokens: both or neither
+    assert reorder(m, st=6 * P, dt=7 * P, nt=5, tc=4) == 2
+    assert reorder(m, dk=P) == 6                  # dst overlaps src
+    assert reorder(m, par=None) == 1
+    assert reorder(m, dk=3 * P + 2) == 4
+    assert reorder(m, W=0) == 0
+
+
+def topk(m, logits=P, cum=None, R=2, W=4, V=1000, kl=8, kg=4, tok=2 * P, par=3 * P, sc=4 * P, ws=8 * P,
+         wsb=None):
+    if wsb is None:
+        wsb = m.beam_topk_workspace_size(R, W, V, kl, kg)
+    return m.lib.bga_beam_topk(logits, cum, R, W, V, kl, kg, tok, par, sc, None, None, None, ws, wsb, None)
+
+
+def test_topk_errors(m):
+    assert m.beam_topk_workspace_size(2, 4, 1000, 8, 4) > 0
+    assert m.beam_topk_workspace_size(2, 4, 1000, 2000, 4) == 0
+    assert topk(m, kl=2000) == 2                  # k_local > V
+    assert topk(m, kg=33) == 2                    # k_global > W * k_local
+    assert topk(m, kl=1025, V=5000) == 3
+    assert topk(m, V=200000) == 3
+    assert topk(m, W=2000) == 3
+    assert topk(m, tok=None) == 1
+    assert topk(m, wsb=16) == 5
+    assert topk(m, ws=None) == 5
+    assert topk(m, logits=P + 2) == 4
+    assert topk(m, R=0) == 0

@@ -1,0 +1,129 @@
+"""Shared-prefix beam decode and parent-index reorder on the GPU against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from helpers import check_bf16, check_lse, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def bga():
+    import attention_bga_packed_amd as m
+    return m
+
+
+def dev(c):
+    return [t.to(DEV) for t in (c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v)]
+
+
+def check_decode(c, ls, name, reqs=None, scale=None):
+    q, pk, pv, sk, sv = dev(c)
+    say(f"[decode] {name} R={c.r} W={c.w} Lp={c.lp} Ls={ls}/{c.ls_cap} nq={c.nq} nkv={c.nkv} d={c.d}")
+    out, lse = bga().shared_prefix_decode(q, pk, pv, sk, sv, ls, scale)
+    torch.cuda.synchronize()
+    reqs = list(range(c.r)) if reqs is None else reqs
+    sl = slice(None)
+    ro, rl = oracle.shared_prefix_decode(c.q[reqs], c.prefix_k[reqs], c.prefix_v[reqs], c.suffix_k[reqs],
+                                         c.suffix_v[reqs], ls, scale)
+    e = check_bf16(out[reqs], ro, f"{name} out")
+    l = check_lse(lse[reqs], rl, f"{name} lse")
+    say(f"    max |out err| {e:.2e}  max |lse err| {l:.2e}")
+    return out, lse
+
+
+@pytest.mark.parametrize("ls", [1, 2, 3, 4])
+def test_short_decode_config(ls):
+    c = wl.make_named_decode("short_decode")
+    check_decode(c, ls, "short_decode")
+
+
+@pytest.mark.parametrize("ls", [1, 5])
+def test_long_beam_decode_config_sampled(ls):
+    c = wl.make_named_decode("long_beam", device=DEV)
+    for f in ("q", "prefix_k", "prefix_v", "suffix_k", "suffix_v"):
+        setattr(c, f, getattr(c, f).cpu())
+    check_decode(c, ls, "long_beam", reqs=[0, 5])
+
+
+@pytest.mark.parametrize("r,w,lp,ls,cap,nq,nkv,d", [
+    (2, 3, 0, 2, 3, 4, 2, 64),       # suffix only
+    (2, 5, 7, 0, 2, 4, 2, 64),       # prefix only, ragged prefix tile
+    (1, 1, 65, 1, 1, 8, 8, 128),     # one beam, MHA
+    (3, 70, 130, 3, 4, 14, 2, 64),   # W*G not a multiple of 128
+    (2, 9, 64, 2, 2, 16, 1, 128),    # group 16
+    (1, 33, 1, 1, 1, 3, 1, 64),      # prefix of one token
+])
+def test_decode_edge_shapes(r, w, lp, ls, cap, nq, nkv, d):
+    c = wl.make_decode_case(r, w, lp, cap, nq, nkv, d, seed=r * 1000 + w + lp)
+    check_decode(c, ls, f"edge r{r} w{w} lp{lp} ls{ls}", scale=0.11)
+
+
+def test_decode_equals_causal_prefill_last_row():
+    """Decode over [prefix; suffix_b] vs the GPU's own causal prefill of that
+    sequence with q_b at the last position (two different kernels)."""
+    c = wl.make_decode_case(1, 4, 90, 3, 4, 2, 64, seed=5)
+    ls = 3
+    q, pk, pv, sk, sv = dev(c)
+    out, lse = bga().shared_prefix_decode(q, pk, pv, sk, sv, ls)
+    for b in range(c.w):
+        n = c.lp + ls
+        kk = torch.cat([pk[0], sk[0, b, :ls]]).contiguous()
+        vv = torch.cat([pv[0], sv[0, b, :ls]]).contiguous()
+        qq = torch.zeros((n, c.nq, c.d), dtype=torch.bfloat16, device=DEV)
+        qq[-1] = q[0, b]
+        cu = torch.tensor([0, n], dtype=torch.int32, device=DEV)
+        op, lp_ = bga().packed_gqa_prefill(qq, kk, vv, cu, n)
+        assert (op[-1].float() - out[0, b].float()).abs().max() <= 1e-2
+        assert (lp_[-1] - lse[0, b]).abs().max() <= 1e-4
+
+
+def test_decode_determinism_and_beam_permutation():
+    c = wl.make_decode_case(2, 37, 100, 2, 4, 2, 64, seed=8)
+    q, pk, pv, sk, sv = dev(c)
+    o1, l1 = bga().shared_prefix_decode(q, pk, pv, sk, sv, 2)
+    o2, l2 = bga().shared_prefix_decode(q, pk, pv, sk, sv, 2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    perm = torch.randperm(c.w, generator=torch.Generator().manual_seed(1)).to(DEV)
+    o3, l3 = bga().shared_prefix_decode(q[:, perm].contiguous(), pk, pv, sk[:, perm].contiguous(),
+                                        sv[:, perm].contiguous(), 2)
+    assert torch.equal(o3, o1[:, perm]) and torch.equal(l3, l1[:, perm])
+
+
+# ---------------------------------------------------------------- reorder
+
+@pytest.mark.parametrize("name,ls", [("short_decode", 4), ("long_beam", 5), ("long_beam", 1)])
+def test_reorder_config_bit_exact(name, ls):
+    cfg = wl.CONFIGS[name]
+    c = wl.make_named_decode(name, device=DEV)
+    parent = wl.make_parents(cfg["r"], cfg["w"], cfg["w"], seed=cfg["seed"] + 10 * ls)
+    tok = torch.from_numpy(np.random.default_rng(ls).integers(0, 151936, (cfg["r"], cfg["w"], 8)).astype(np.int32))
+    say(f"[reorder] {name} Ls={ls}")
+    pdev = torch.from_numpy(parent).to(DEV)
+    dk = torch.full_like(c.suffix_k, 3.0)
+    dv = torch.full_like(c.suffix_v, 3.0)
+    dk, dv, dt = bga().suffix_reorder(c.suffix_k, c.suffix_v, pdev, ls, dst_k=dk, dst_v=dv,
+                                      src_tokens=tok.to(DEV), num_tokens=ls)
+    rk, rv, rt = oracle.suffix_reorder(c.suffix_k.cpu(), c.suffix_v.cpu(), parent, ls, tok.numpy(), ls)
+    gk = dk.cpu().view(torch.int16).numpy().view(np.uint16)
+    gv = dv.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gk[:, :, :ls], rk[:, :, :ls]) and np.array_equal(gv[:, :, :ls], rv[:, :, :ls])
+    # positions >= suffix_len untouched
+    assert torch.all(dk[:, :, ls:] == 3.0) and torch.all(dv[:, :, ls:] == 3.0)
+    assert np.array_equal(dt.cpu().numpy()[:, :, :ls], rt[:, :, :ls])
+
+
+def test_reorder_identity_and_bad_parent():
+    c = wl.make_decode_case(2, 6, 4, 3, 4, 2, 64, seed=2)
+    sk, sv = c.suffix_k.to(DEV), c.suffix_v.to(DEV)
+    ident = torch.arange(6, dtype=torch.int32, device=DEV).repeat(2, 1)
+    dk, dv = bga().suffix_reorder(sk, sv, ident, 3)
+    assert torch.equal(dk, sk) and torch.equal(dv, sv)
+    bad = ident.clone()
+    bad[1, 2] = 99
+    dk, dv = bga().suffix_reorder(sk, sv, bad, 3)
+    assert torch.all(dk[1, 2] == 0) and torch.equal(dk[0], sk[0]) and torch.equal(dk[1, 3], sk[1, 3])
