@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over synthetic inputs:
+  * a Prefill-Only request: 28 launches (one per layer) of packed causal GQA
+    prefill over 15 packed sequences, lengths uniform in [64, 480] (T = 4228),
+    16 query / 8 KV heads, head dim 128, each layer with its own Q/K/V;
+  * a long-prompt beam search: 8 requests x 400 beams over a 480-token shared
+    prompt, 5 decode steps, each = shared-prefix decode (16/8 heads, d 128,
+    suffix length = step) -> two-stage top-K over bf16 logits [8, 400, 151936]
+    (2W per beam, W overall) -> parent-index suffix K/V reorder.
+
+The headline value is the prefill attention throughput in logical TFLOP/s
+(4 * D * Nq * sum L(L+1)/2 per layer, FMA = 2); decode, top-K and reorder are
+reported in algorithmic GB/s. Kernel times come from HIP events around every
+launch on the launching stream. Inputs are drawn on the GPU from fixed seeds.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget for the oracle baseline sample (0 disables it)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the hot path is measured on a single MI355X and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- inputs (resident in HBM before timing)
+    pcfg = wl.CONFIGS["prefill_only"]
+    lengths = wl.prefill_lengths(pcfg)
+    layers = pcfg["layers"]
+    cases = [wl.make_prefill_case(lengths, pcfg["nq"], pcfg["nkv"], pcfg["d"], pcfg["seed"] * 1000 + i, dev)
+             for i in range(layers)]
+    cu = torch.from_numpy(cases[0].cu_seqlens).to(dev)
+    max_len = max(lengths)
+    p_out = torch.empty_like(cases[0].q)
+    p_lse = torch.empty(cases[0].q.shape[:2], dtype=torch.float32, device=dev)
+
+    bcfg = wl.CONFIGS["long_beam"]
+    R, W, LP, NS, NQ, NKV, D, V = (bcfg[k] for k in ("r", "w", "lp", "steps", "nq", "nkv", "d", "vocab"))
+    dc = wl.make_named_decode("long_beam", device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(bcfg["seed"] * 7919)
+    qs = [wl.bf16_normal((R, W, NQ, D), gen, dev) for _ in range(NS)]
+    logits = [wl.make_logits(R, W, V, bcfg["logit_std"], bcfg["seed"] + s + 1, dev) for s in range(NS)]
+    suf = [(dc.suffix_k, dc.suffix_v), (torch.empty_like(dc.suffix_k), torch.empty_like(dc.suffix_v))]
+    d_out = torch.empty_like(qs[0])
+    d_lse = torch.empty((R, W, NQ), dtype=torch.float32, device=dev)
+    ws = torch.empty(bga.beam_topk_workspace_size(R, W, V, 2 * W, W), dtype=torch.uint8, device=dev)
+    topk_out = {"tokens": torch.empty((R, W), dtype=torch.int32, device=dev),
+                "parents": torch.empty((R, W), dtype=torch.int32, device=dev),
+                "scores": torch.empty((R, W), dtype=torch.float32, device=dev)}
+    cum = torch.zeros((R, W), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    n_ev = layers + 3 * NS
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+
+    def step():
+        i = 0
+        for c in cases:
+            evs[i][0].record(stream)
+            bga.packed_gqa_prefill(c.q, c.k, c.v, cu, max_len, out=p_out, lse=p_lse)
+            evs[i][1].record(stream)
+            i += 1
+        cur = 0
+        cum.zero_()
+        for s in range(NS):
+            sk, sv = suf[cur]
+            evs[i][0].record(stream)
+            bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=d_out, lse=d_lse)
+            evs[i][1].record(stream)
+            evs[i + 1][0].record(stream)
+            bga.beam_topk(logits[s], cum, 2 * W, W, workspace=ws, out=topk_out)
+            evs[i + 1][1].record(stream)
+            evs[i + 2][0].record(stream)
+            nk, nv = suf[1 - cur]
+            bga.suffix_reorder(sk, sv, topk_out["parents"], s + 1, dst_k=nk, dst_v=nv)
+            evs[i + 2][1].record(stream)
+            cum.copy_(topk_out["scores"])
+            cur = 1 - cur
+            i += 3
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t_pre = [0.0] * layers
+    t_dec = [0.0] * NS
+    t_top = [0.0] * NS
+    t_reo = [0.0] * NS
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+        torch.cuda.synchronize()   # events of this step are complete; read them
+        for l in range(layers):
+            t_pre[l] += evs[l][0].elapsed_time(evs[l][1])
+        for s in range(NS):
+            j = layers + 3 * s
+            t_dec[s] += evs[j][0].elapsed_time(evs[j][1])
+            t_top[s] += evs[j + 1][0].elapsed_time(evs[j + 1][1])
+            t_reo[s] += evs[j + 2][0].elapsed_time(evs[j + 2][1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    K = args.steps
+    pre_flops = wl.prefill_flops(lengths, pcfg["nq"], pcfg["d"])
+    pre_ms = sum(t_pre) / (K * layers)                      # average launch, ms
+    pre_tflops = pre_flops / (pre_ms * 1e-3) / 1e12
+    dec_bytes = [wl.decode_bytes(R, W, NQ, NKV, LP, s + 1, D) for s in range(NS)]
+    dec_ms = [t / K for t in t_dec]
+    dec_gbs = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
+    dec_flops = sum(wl.decode_flops(R, W, NQ, LP, s + 1, D) for s in range(NS))
+    top_bytes = wl.topk_bytes(R, W, V, W)
+    top_ms = sum(t_top) / (K * NS)
+    top_gbs = top_bytes / (top_ms * 1e-3) / 1e9
+    reo_bytes = [wl.reorder_bytes(R, W, s + 1, NKV, D) for s in range(NS)]
+    reo_ms = [t / K for t in t_reo]
+    reo_gbs = sum(reo_bytes) / (sum(reo_ms) * 1e-3) / 1e9
+
+    def roof(bound, achieved, peak, unit, per_launch, ms):
+        return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "algorithmic_per_launch": per_launch, "avg_launch_us": round(ms * 1e3, 2)}
+
+    rooflines = {
+        "packed_gqa_prefill": roof("mfma", pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre_flops, pre_ms),
+        "shared_prefix_decode": roof("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_bytes)),
+                                     float(np.mean(dec_ms))),
+        "beam_topk": roof("hbm", top_gbs, PEAK_HBM_GBS, "GB/s", top_bytes, top_ms),
+        "suffix_reorder": roof("hbm", reo_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(reo_bytes)),
+                               float(np.mean(reo_ms))),
+    }
+    rooflines["shared_prefix_decode"]["mfma_tflops"] = round(dec_flops / (sum(dec_ms) * 1e-3) / 1e12, 2)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cases[0], pre_flops, args.cpu_seconds)
+
+    rec = {
+        "metric": "attention TFLOPS & %bf16 MFMA peak (prefill); GB/s & %HBM peak (beam decode)",
+        "value": round(pre_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,3) logits; no weights)",
+        "config": {
+            "workload": "prefill_only x28 layers + long_beam 5-step beam search",
+            "prefill": {"sequences": len(lengths), "total_tokens": int(sum(lengths)), "max_len": max_len,
+                        "num_q_heads": pcfg["nq"], "num_kv_heads": pcfg["nkv"], "head_dim": pcfg["d"],
+                        "launches_per_step": layers},
+            "beam": {"requests": R, "beams": W, "prefix_len": LP, "decode_steps": NS, "num_q_heads": NQ,
+                     "num_kv_heads": NKV, "head_dim": D, "vocab": V, "k_local": 2 * W, "k_global": W},
+            "global_batch": len(lengths),
+            "seq_len": max_len,
+        },
+        "prefill_pct_bf16_peak": round(100 * pre_tflops / PEAK_BF16_TFLOPS, 2),
+        "decode_gbs": round(dec_gbs, 1),
+        "decode_pct_hbm_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
+        "decode_us_per_step": [round(t * 1e3, 2) for t in dec_ms],
+        "topk_gbs": round(top_gbs, 1),
+        "reorder_gbs": round(reo_gbs, 1),
+        "roofline": rooflines["packed_gqa_prefill"],
+        "rooflines": rooflines,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(case, flops, seconds):
+    """The fp64 oracle on one Prefill-Only layer, repeated until ~`seconds` of CPU work."""
+    import oracle
+    import numpy as np
+
+    q, k, v = case.q.cpu(), case.k.cpu(), case.v.cpu()
+    cu = np.asarray(case.cu_seqlens)
+    threads = oracle.num_threads(0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.packed_prefill(q, k, v, cu, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": round(flops * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x one Prefill-Only layer (15 sequences, T={int(cu[-1])}, 16/8 heads, d 128) "
+                      f"in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
