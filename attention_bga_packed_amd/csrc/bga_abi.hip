@@ -4,7 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/bga.h"
+#include "bga.h"
 #include "internal.hpp"
 
 namespace {

@@ -25,7 +25,7 @@
 namespace bga {
 
 template <int D>
-__global__ __launch_bounds__(256) void shared_prefix_decode_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void shared_prefix_decode_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ pk, const uint16_t *__restrict__ pv,
     const uint16_t *__restrict__ sk, const uint16_t *__restrict__ sv, int W, int Lp, int Ls, int Ls_cap, int nq,
     int nkv, int group, float scale, uint16_t *__restrict__ out, float *__restrict__ lse)
@@ -48,30 +48,20 @@ __global__ __launch_bounds__(256) void shared_prefix_decode_kernel(
     bf16x8 qop[D / 16];
     load_q_operand<D>(qop, q + qrow_idx * D, row_valid);
 
+    const BGA_LDS char *lds = lds_ptr(smem);
+    const uint32_t lds_base = lds_addr(lds);
     WaveAttn<D> st;
-    st.init();
+    st.init(lds);
     const float c2 = scale * kLog2e;
 
     // ---- prefix segment: MFMA tiles through LDS, shared by the 4 waves
-    const size_t row_stride = (size_t)nkv * D;
-    const uint16_t *kbase = pk + (size_t)r * Lp * row_stride + (size_t)g * D;
-    const uint16_t *vbase = pv + (size_t)r * Lp * row_stride + (size_t)g * D;
-    const int nkt = (Lp + T::BN - 1) / T::BN;
-    T tl;
-    if (nkt > 0) {
-        tl.load(kbase, vbase, row_stride, 0, Lp, tid, nthr);
-        tl.store(smem, tid, nthr);
-    }
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int kstart = kt * T::BN;
-        if (kt + 1 < nkt) tl.load(kbase, vbase, row_stride, kstart + T::BN, Lp, tid, nthr);
-        __syncthreads();
-        if (wave_active) {
-            const uint16_t *Ks = smem + (kt & 1) * T::STAGE;
-            st.tile(Ks, Ks + T::K_ELEMS, qop, c2, kstart + T::BN > Lp, kstart, Lp - 1);
-        }
-        if (kt + 1 < nkt) tl.store(smem + ((kt + 1) & 1) * T::STAGE, tid, nthr);
-    }
+    const uint32_t row_stride = (uint32_t)(nkv * D);
+    DmaPlan<D> plan;
+    plan.init(w, nthr >> 6, row_stride);
+    const size_t pbase = (size_t)r * Lp * row_stride + (size_t)g * D;
+    const int nkt = (Lp + AttnTile<D>::BN - 1) / AttnTile<D>::BN;
+    attn_scan<D>(st, plan, lds_base, qop, pk + pbase, pv + pbase, row_stride, 0, Lp, nkt, c2,
+                 [&](int kt) { return (kt + 1) * AttnTile<D>::BN > Lp; }, Lp - 1);
     if (!wave_active) return;
 
     // ---- suffix segment: this beam's own keys, folded into the same state
@@ -91,7 +81,7 @@ __global__ __launch_bounds__(256) void shared_prefix_decode_kernel(
                 part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(kv[e]), part);
             }
         }
-        const float s = part + xor32(part);
+        const float s = pair_sum(part);
         const float m_new = fmaxf(st.m, s);
         const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);
         const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);

@@ -39,9 +39,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// value of the lane 32 positions away (lanes l and l ^ 32)
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
-
 __device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll

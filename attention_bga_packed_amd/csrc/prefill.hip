@@ -26,7 +26,7 @@
 namespace bga {
 
 template <int D>
-__global__ __launch_bounds__(512) void packed_prefill_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void packed_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, int nq, int nkv, int group, int hsplit, int hpw, int ts_per_wg, float scale,
     uint16_t *__restrict__ out, float *__restrict__ lse)
@@ -43,40 +43,31 @@ __global__ __launch_bounds__(512) void packed_prefill_kernel(
     const int kend = min(q_lo + bm, s1);
     const int nkt = (kend - s0 + T::BN - 1) / T::BN;
 
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int w = tid >> 6, lane = tid & 63, col = lane & 31;
+    const int nthr = blockDim.x;
+    const int w = threadIdx.x >> 6, col = threadIdx.x & 31;
     const int hig = split * hpw + (w % hpw);   // head within the group
     const int head = g * group + min(hig, group - 1);
     const int qw0 = q_lo + (w / hpw) * 32;
     const int qtok = qw0 + col;
     const bool wave_active = qw0 < s1 && hig < group;
     const bool row_valid = qtok < s1 && wave_active;
-    const int wave_last_q = min(qw0 + 31, s1 - 1);
 
     bf16x8 qop[D / 16];
     load_q_operand<D>(qop, q + ((size_t)qtok * nq + head) * D, row_valid);
 
+    const BGA_LDS char *lds = lds_ptr(smem);
+    const uint32_t lds_base = lds_addr(lds);
     WaveAttn<D> st;
-    st.init();
+    st.init(lds);
     const float c2 = scale * kLog2e;
-
-    const size_t row_stride = (size_t)nkv * D;
-    const uint16_t *kbase = k + (size_t)g * D;
-    const uint16_t *vbase = v + (size_t)g * D;
-
-    T tl;
-    tl.load(kbase, vbase, row_stride, s0, kend, tid, nthr);
-    tl.store(smem, tid, nthr);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int kstart = s0 + kt * T::BN;
-        if (kt + 1 < nkt) tl.load(kbase, vbase, row_stride, kstart + T::BN, kend, tid, nthr);
-        __syncthreads();
-        if (wave_active && kstart <= wave_last_q) {
-            const uint16_t *Ks = smem + (kt & 1) * T::STAGE;
-            st.tile(Ks, Ks + T::K_ELEMS, qop, c2, kstart + T::BN - 1 > qw0, kstart, qtok);
-        }
-        if (kt + 1 < nkt) tl.store(smem + ((kt + 1) & 1) * T::STAGE, tid, nthr);
-    }
+    const uint32_t row_stride = (uint32_t)(nkv * D);
+    DmaPlan<D> plan;
+    plan.init(w, nthr >> 6, row_stride);
+    // tile kt needs masking when it reaches past this wave's first query; tiles
+    // entirely after the wave's last query are fully masked (contribute zero)
+    auto need_mask = [&](int kt) { return s0 + kt * AttnTile<D>::BN + AttnTile<D>::BN - 1 > qw0; };
+    attn_scan<D>(st, plan, lds_base, qop, k + (size_t)g * D, v + (size_t)g * D, row_stride, s0, kend, nkt, c2,
+                 need_mask, qtok);
     if (!wave_active) return;
     st.finish(out + ((size_t)qtok * nq + head) * D, lse ? lse + (size_t)qtok * nq + head : nullptr, row_valid,
               scale);
