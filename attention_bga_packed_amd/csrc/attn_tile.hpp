@@ -237,6 +237,13 @@ struct WaveAttn {
                 const u32x4 a = *(const BGA_LDS u32x4 *)(kofs[ks] + (KSLOT + kb * 32 * T::ROWB));
                 s[kb] = mfma32x32x16(as_bf16x8(a), qop[ks], s[kb]);
             }
+        // K reads run two MFMAs ahead, no further (bounded register pressure)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
     }
 
     // The fused step body (no branches): scores of the next tile into sn from

@@ -30,6 +30,42 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM bytes per launch, from two rocprofv3 --pmc passes over this script (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches). Calibration: a plain 512 MiB
+# device copy (--calib-copy-mb 512) reads FETCH_SIZE = 262156 KiB and WRITE_SIZE = 524288 KiB, so
+# fetch counts are scaled by 2 and write counts by 1 (beam_topk: both of its kernels). Each figure is tied to the sources of the
+# kernel it was measured on and is reported as null once they change.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+KERNEL_SOURCES = {
+    "packed_gqa_prefill": ["prefill.hip", "attn_tile.hpp", "device_common.hpp", "internal.hpp"],
+    "shared_prefix_decode": ["decode.hip", "attn_tile.hpp", "device_common.hpp", "internal.hpp"],
+    "beam_topk": ["topk.hip", "device_common.hpp", "internal.hpp"],
+    "suffix_reorder": ["reorder.hip", "internal.hpp"],
+}
+MEASURED_TRAFFIC = {
+    "packed_gqa_prefill": {"fetch_kib": 18509.2, "write_kib": 19158.1, "sources_sha256": "d5fbe6c590a4a171"},
+    "shared_prefix_decode": {"fetch_kib": 35157.6, "write_kib": 17632.0, "sources_sha256": "dd75cbce1954c050"},
+    "beam_topk": {"fetch_kib": 950790.1, "write_kib": 20037.5, "sources_sha256": "fadf4f07e1cff4bc"},
+    "suffix_reorder": {"fetch_kib": 15208.8, "write_kib": 38400.0, "sources_sha256": "64b133c74e63f310"},
+}
+
+
+def sources_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["../build.py"]:
+        with open(os.path.join(ROOT, "attention_bga_packed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """Counter-derived HBM bytes per launch, or None if not measured on the current sources."""
+    t = MEASURED_TRAFFIC.get(kernel)
+    if t is None or t["sources_sha256"] != sources_sha(kernel):
+        return None
+    return int(round(t["fetch_kib"] * 1024 * FETCH_SCALE + t["write_kib"] * 1024 * WRITE_SCALE))
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -38,6 +74,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget for the oracle baseline sample (0 disables it)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a known-size dispatch "
+                         "for calibrating the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -86,47 +125,83 @@ def main():
     cum = torch.zeros((R, W), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    if args.calib_copy_mb > 0:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     stream = torch.cuda.current_stream(dev)
     n_ev = layers + 3 * NS
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
 
-    def step():
+    def step(timed):
+        """One pass of the hot path; with `timed`, HIP events bracket every launch."""
         i = 0
         for c in cases:
-            evs[i][0].record(stream)
+            if timed:
+                evs[i][0].record(stream)
             bga.packed_gqa_prefill(c.q, c.k, c.v, cu, max_len, out=p_out, lse=p_lse)
-            evs[i][1].record(stream)
+            if timed:
+                evs[i][1].record(stream)
             i += 1
         cur = 0
         cum.zero_()
         for s in range(NS):
             sk, sv = suf[cur]
-            evs[i][0].record(stream)
-            bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=d_out, lse=d_lse)
-            evs[i][1].record(stream)
-            evs[i + 1][0].record(stream)
-            bga.beam_topk(logits[s], cum, 2 * W, W, workspace=ws, out=topk_out)
-            evs[i + 1][1].record(stream)
-            evs[i + 2][0].record(stream)
             nk, nv = suf[1 - cur]
-            bga.suffix_reorder(sk, sv, topk_out["parents"], s + 1, dst_k=nk, dst_v=nv)
-            evs[i + 2][1].record(stream)
+            launches = (
+                lambda: bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=d_out, lse=d_lse),
+                lambda: bga.beam_topk(logits[s], cum, 2 * W, W, workspace=ws, out=topk_out),
+                lambda: bga.suffix_reorder(sk, sv, topk_out["parents"], s + 1, dst_k=nk, dst_v=nv),
+            )
+            for j, fn in enumerate(launches):
+                if timed:
+                    evs[i + j][0].record(stream)
+                fn()
+                if timed:
+                    evs[i + j][1].record(stream)
             cum.copy_(topk_out["scores"])
             cur = 1 - cur
             i += 3
 
     for _ in range(args.warmup):
-        step()
+        step(True)
     torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, wall clock
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # ---- per-kernel durations: the same K steps again, HIP events around every launch on the
+    # launching stream. A spin kernel queued first holds the GPU while the host enqueues the whole
+    # step, so the launches run back to back and each event pair spans only its kernel (otherwise
+    # the host's per-launch overhead, which exceeds a prefill launch, would be counted too).
+    host_t = time.perf_counter()
+    step(True)
+    host_t = time.perf_counter() - host_t
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
+    gate = int(cycles_per_ms * max(3.0 * host_t * 1e3, 2.0))
 
     t_pre = [0.0] * layers
     t_dec = [0.0] * NS
     t_top = [0.0] * NS
     t_reo = [0.0] * NS
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        torch.cuda._sleep(gate)
+        step(True)
         torch.cuda.synchronize()   # events of this step are complete; read them
         for l in range(layers):
             t_pre[l] += evs[l][0].elapsed_time(evs[l][1])
@@ -135,8 +210,6 @@ def main():
             t_dec[s] += evs[j][0].elapsed_time(evs[j][1])
             t_top[s] += evs[j + 1][0].elapsed_time(evs[j + 1][1])
             t_reo[s] += evs[j + 2][0].elapsed_time(evs[j + 2][1])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     K = args.steps
     pre_flops = wl.prefill_flops(lengths, pcfg["nq"], pcfg["d"])
@@ -153,17 +226,17 @@ def main():
     reo_ms = [t / K for t in t_reo]
     reo_gbs = sum(reo_bytes) / (sum(reo_ms) * 1e-3) / 1e9
 
-    def roof(bound, achieved, peak, unit, per_launch, ms):
+    def roof(kernel, bound, achieved, peak, unit, per_launch, ms):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel),
                 "algorithmic_per_launch": per_launch, "avg_launch_us": round(ms * 1e3, 2)}
 
     rooflines = {
-        "packed_gqa_prefill": roof("mfma", pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre_flops, pre_ms),
-        "shared_prefix_decode": roof("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_bytes)),
+        "packed_gqa_prefill": roof("packed_gqa_prefill", "mfma", pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre_flops, pre_ms),
+        "shared_prefix_decode": roof("shared_prefix_decode", "hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_bytes)),
                                      float(np.mean(dec_ms))),
-        "beam_topk": roof("hbm", top_gbs, PEAK_HBM_GBS, "GB/s", top_bytes, top_ms),
-        "suffix_reorder": roof("hbm", reo_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(reo_bytes)),
+        "beam_topk": roof("beam_topk", "hbm", top_gbs, PEAK_HBM_GBS, "GB/s", top_bytes, top_ms),
+        "suffix_reorder": roof("suffix_reorder", "hbm", reo_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(reo_bytes)),
                                float(np.mean(reo_ms))),
     }
     rooflines["shared_prefix_decode"]["mfma_tflops"] = round(dec_flops / (sum(dec_ms) * 1e-3) / 1e12, 2)
