@@ -41,16 +41,23 @@ namespace bga {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// One global_load_lds_dwordx4: 64 lanes x 16 bytes from per-lane global
-// addresses into 1 KB of LDS at byte address `lds_dst` (+16 * lane). Written as
+// One global_load_lds_dwordx4: 64 lanes x 16 bytes from global addresses
+// sbase + voff (a wave-uniform base and a per-lane byte offset) into 1 KB of
+// LDS at byte address `lds_dst` (+16 * lane). Written as
 // inline assembly so that the compiler does not treat the in-flight copy as
 // aliasing every later LDS read (which would make it wait for the copy
 // mid-tile); the callers wait for completion themselves (s_waitcnt vmcnt(0) +
 // barrier) before any wave reads the slot.
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_dst)
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds_dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+    const uint64_t a = (uint64_t)(size_t)sbase;
+    // readfirstlane yields a signed int: widen through uint32_t (no sign extension)
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t sa = lo | (hi << 32);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sa), "s"(m0)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ const BGA_LDS char *lds_ptr(const void *p) { return (const BGA_LDS char *)p; }
@@ -83,30 +90,37 @@ struct AttnTile {
     static constexpr uint32_t vslot(int j) { return (uint32_t)((2 + j) * KBYTES); }
 };
 
-// This wave's share of the copies of one tile, precomputed per lane: copy j of
-// the wave is instruction i = wave + j * nwaves of the tile; it moves row
-// row[j] (0..63) of the tile, chunk-swizzled, into bytes dst[j] of the slot.
-template <int D>
+// This wave's share of the copies of one tile: copy j of the wave is
+// instruction i = wave + j * nwaves of the tile; it moves tile row row(j)
+// (0..63), chunk-swizzled, into bytes i * 1 KB of the slot. Each lane keeps
+// its byte offset within the row (the swizzled chunk); the row offset goes
+// into the wave-uniform base wherever possible. NW is the number of waves when
+// known at compile time (0: run-time). When NW copies cover a multiple of 16
+// rows, row(j) - row(0) is a multiple of 16, the swizzle of every copy equals
+// that of copy 0, and one set of per-lane values serves all copies.
+template <int D, int NW = 0>
 struct DmaPlan {
     using T = AttnTile<D>;
-    int wave, nwaves, n;                     // wave-uniform: copies this wave issues per tile
-    int row[T::MAXI];
-    uint32_t koff[T::MAXI], voff[T::MAXI];   // element offsets (row * row_stride + chunk * 8)
+    static constexpr bool kStrided = NW > 0 && (NW * T::RPI) % 16 == 0;
+    static constexpr int kSlots = kStrided ? 1 : T::MAXI;
+    int wave, nwaves, n;                 // wave-uniform: copies this wave issues per tile
+    int row[kSlots];                     // tile row of copy j (kStrided: of copy 0)
+    uint32_t kch[kSlots], vch[kSlots];   // byte offset of this lane's 16 bytes within the K / V row
 
-    __device__ __forceinline__ void init(int wave_, int nwaves_, uint32_t row_stride)
+    __device__ __forceinline__ void init(int wave_, int nwaves_)
     {
         const int lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(wave_);
-        nwaves = __builtin_amdgcn_readfirstlane(nwaves_);
+        nwaves = NW > 0 ? NW : __builtin_amdgcn_readfirstlane(nwaves_);
         n = 0;
 #pragma unroll
-        for (int j = 0; j < T::MAXI; ++j) {
-            const int i = wave + j * nwaves;
-            const int r = i * T::RPI + lane / T::CHUNKS, pc = lane % T::CHUNKS;
+        for (int j = 0; j < T::MAXI; ++j) n += wave + j * nwaves < T::DMA;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            const int r = (wave + j * nwaves) * T::RPI + lane / T::CHUNKS, pc = lane % T::CHUNKS;
             row[j] = r;
-            koff[j] = (uint32_t)r * row_stride + (uint32_t)((pc ^ T::swk(r)) * 8);
-            voff[j] = (uint32_t)r * row_stride + (uint32_t)((pc ^ T::swv(r)) * 8);
-            n += i < T::DMA;
+            kch[j] = (uint32_t)((pc ^ T::swk(r)) * 16);
+            vch[j] = (uint32_t)((pc ^ T::swv(r)) * 16);
         }
     }
 
@@ -116,20 +130,30 @@ struct DmaPlan {
     __device__ __forceinline__ void issue(uint32_t slot, const uint16_t *__restrict__ base, uint32_t row_stride,
                                           int kstart, int kend, bool is_v) const
     {
-        const uint16_t *b = base + (size_t)kstart * row_stride;
-        if (kstart + T::BN <= kend) {
+        const char *b = (const char *)(base + (size_t)kstart * row_stride);
+        const uint32_t rbytes = row_stride * 2;
+        const bool full = kstart + T::BN <= kend;
+        const int last = kend - 1 - kstart;   // last valid tile row
 #pragma unroll
-            for (int j = 0; j < T::MAXI; ++j)
-                if (j < n) lds_dma16(b + (is_v ? voff[j] : koff[j]), slot + (uint32_t)((wave + j * nwaves) * 1024));
-        } else {
-#pragma unroll
-            for (int j = 0; j < T::MAXI; ++j)
-                if (j < n) {
-                    const int over = kstart + row[j] - (kend - 1);
-                    const uint32_t off = (is_v ? voff[j] : koff[j]) - (over > 0 ? (uint32_t)over * row_stride : 0u);
-                    lds_dma16(b + off, slot + (uint32_t)((wave + j * nwaves) * 1024));
+        for (int j = 0; j < T::MAXI; ++j)
+            if (j < n) {
+                const int s = kStrided ? 0 : j;
+                const uint32_t ch = is_v ? vch[s] : kch[s];
+                const uint32_t dst = slot + (uint32_t)((wave + j * nwaves) * 1024);
+                if constexpr (kStrided) {
+                    // copy j = copy 0 moved down by j * NW * RPI rows
+                    const int dr = j * NW * T::RPI;
+                    if (full) {
+                        lds_dma16(b + (size_t)dr * rbytes, (uint32_t)row[0] * rbytes + ch, dst);
+                    } else {
+                        const int r = min(row[0] + dr, last);
+                        lds_dma16(b, (uint32_t)r * rbytes + ch, dst);
+                    }
+                } else {
+                    const int r = full ? row[j] : min(row[j], last);
+                    lds_dma16(b, (uint32_t)r * rbytes + ch, dst);
                 }
-        }
+            }
     }
 };
 
@@ -157,7 +181,8 @@ struct WaveAttn {
 
     static constexpr float kLazy = 8.f;   // log2 of the largest unnormalised probability kept
 
-    __device__ __forceinline__ void init(const BGA_LDS char *lds_base)
+    // empty state: no keys seen
+    __device__ __forceinline__ void reset()
     {
 #pragma unroll
         for (int b = 0; b < D / 32; ++b)
@@ -165,6 +190,11 @@ struct WaveAttn {
             for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
         m = -INFINITY;
         l = 0.f;
+    }
+
+    __device__ __forceinline__ void init(const BGA_LDS char *lds_base)
+    {
+        reset();
         const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
         // rows col and col + 32 share the K swizzle (it looks at the low four bits only)
 #pragma unroll
@@ -340,22 +370,33 @@ __device__ __forceinline__ void load_q_operand(bf16x8 *qop, const uint16_t *qrow
 struct Parity0 { static constexpr int value = 0; };
 struct Parity1 { static constexpr int value = 1; };
 
+// Copies of the first tile's K and V into slots 0 (the scan's prologue; a
+// caller may issue them early and pass first_issued = true to the scan).
+template <int D, typename Plan>
+__device__ __forceinline__ void attn_scan_first(const Plan &plan, uint32_t lds_base, const uint16_t *kbase,
+                                                const uint16_t *vbase, uint32_t row_stride, int key0, int kend)
+{
+    using T = AttnTile<D>;
+    plan.issue(lds_base + T::kslot(0), kbase, row_stride, key0, kend, false);
+    plan.issue(lds_base + T::vslot(0), vbase, row_stride, key0, kend, true);
+}
+
 // The double-buffered scan over tiles [0, nkt) shared by both kernels.
 // Tile kt holds keys [key0 + 64*kt, key0 + 64*kt + 64); K/V row `key` lives at
 // kbase/vbase + key * row_stride; keys >= kend are clamped. need_mask(kt) says
 // whether tile kt is masked (keys > mask_limit). Every wave of the workgroup
 // must call this (it contains barriers); waves without work compute on
-// whatever their inputs are and discard the result.
-template <int D, typename NeedMask>
-__device__ __forceinline__ void attn_scan(WaveAttn<D> &st, const DmaPlan<D> &plan, uint32_t lds_base,   // LDS byte address
+// whatever their inputs are and discard the result. The state st may already
+// hold keys folded in by the caller.
+template <int D, typename Plan, typename NeedMask>
+__device__ __forceinline__ void attn_scan(WaveAttn<D> &st, const Plan &plan, uint32_t lds_base,   // LDS byte address
                                           const bf16x8 *qop, const uint16_t *kbase, const uint16_t *vbase,
                                           uint32_t row_stride, int key0, int kend, int nkt, float c2,
-                                          NeedMask need_mask, int mask_limit)
+                                          NeedMask need_mask, int mask_limit, bool first_issued = false)
 {
     using T = AttnTile<D>;
     if (nkt <= 0) return;
-    plan.issue(lds_base + T::kslot(0), kbase, row_stride, key0, kend, false);
-    plan.issue(lds_base + T::vslot(0), vbase, row_stride, key0, kend, true);
+    if (!first_issued) attn_scan_first<D>(plan, lds_base, kbase, vbase, row_stride, key0, kend);
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
     if (nkt > 1) plan.issue(lds_base + T::kslot(1), kbase, row_stride, key0 + T::BN, kend, false);

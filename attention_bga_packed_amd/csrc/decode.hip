@@ -36,17 +36,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int rg = blockIdx.x;
     const int r = rg / nkv, g = rg % nkv;
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const int w = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int w = tid >> 6;
     const int rows = W * group;
-    const int n = blockIdx.y * 128 + w * 32 + col;  // query row within (r, g): beam * G + head-in-group
-    const bool row_valid = n < rows;
-    const int beam = row_valid ? n / group : 0;
-    const int head = g * group + (row_valid ? n % group : 0);
     const bool wave_active = blockIdx.y * 128 + w * 32 < rows;
-    const size_t qrow_idx = ((size_t)r * W + beam) * nq + head;
+
+    // query row within (r, g): beam * G + head-in-group
+    auto query_row = [&](bool &valid, int &beam) {
+        const int n = blockIdx.y * 128 + w * 32 + (threadIdx.x & 31);
+        valid = n < rows;
+        beam = valid ? n / group : 0;
+        const int head = g * group + (valid ? n % group : 0);
+        return ((size_t)r * W + beam) * nq + head;
+    };
 
     bf16x8 qop[D / 16];
-    load_q_operand<D>(qop, q + qrow_idx * D, row_valid);
+    {
+        bool valid;
+        int beam;
+        const size_t qi = query_row(valid, beam);
+        load_q_operand<D>(qop, q + qi * D, valid);
+    }
 
     const BGA_LDS char *lds = lds_ptr(smem);
     const uint32_t lds_base = lds_addr(lds);
@@ -54,51 +63,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     st.init(lds);
     const float c2 = scale * kLog2e;
 
+    // the row's indices (recomputed where needed: fewer registers live across the scan)
+    const int half = (threadIdx.x & 63) >> 5;
+
+    // ---- suffix segment: this beam's own keys, folded into the same state
+    // (invalid query rows read beam 0's rows, which exist, and are dropped at the end)
+    struct SuffixKey {
+        u32x4 k[D / 16];      // K row: this lane's d-half of every 16-wide d step
+        u32x2 v[D / 32][4];   // V row: the d values this lane accumulates
+    };
+    auto suffix = [&]() {   // after the prefix scan (its registers are free by then)
+        bool valid;
+        int beam;
+        query_row(valid, beam);
+        const size_t sbase = (((size_t)r * W + beam) * Ls_cap * nkv + g) * D;
+        const uint32_t rs = (uint32_t)(nkv * D);
+        for (int j = 0; j < Ls; ++j) {
+            SuffixKey x;
+            const uint16_t *kr = sk + sbase + (size_t)j * rs, *vr = sv + sbase + (size_t)j * rs;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) x.k[ks] = *(const u32x4 *)(kr + ks * 16 + half * 8);
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int rgi = 0; rgi < 4; ++rgi) x.v[b][rgi] = *(const u32x2 *)(vr + b * 32 + rgi * 8 + half * 4);
+            float part = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(x.k[ks][e]), part);
+                    part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(x.k[ks][e]), part);
+                }
+            }
+            const float s = pair_sum(part);
+            const float m_new = fmaxf(st.m, s);
+            const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);   // 0 on the first key (m = -inf)
+            const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
+            st.l = st.l * alpha + (half == 0 ? p : 0.f);
+            st.m = m_new;
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int rgi = 0; rgi < 4; ++rgi) {
+                    const u32x2 vv = x.v[b][rgi];
+                    st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
+                    st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
+                    st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
+                    st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
+                }
+        }
+    };
+
     // ---- prefix segment: MFMA tiles through LDS, shared by the 4 waves
     const uint32_t row_stride = (uint32_t)(nkv * D);
-    DmaPlan<D> plan;
-    plan.init(w, nthr >> 6, row_stride);
+    DmaPlan<D, 4> plan;   // 4 waves per workgroup
+    plan.init(w, nthr >> 6);
     const size_t pbase = (size_t)r * Lp * row_stride + (size_t)g * D;
     const int nkt = (Lp + AttnTile<D>::BN - 1) / AttnTile<D>::BN;
     attn_scan<D>(st, plan, lds_base, qop, pk + pbase, pv + pbase, row_stride, 0, Lp, nkt, c2,
                  [&](int kt) { return (kt + 1) * AttnTile<D>::BN > Lp; }, Lp - 1);
     if (!wave_active) return;
-
-    // ---- suffix segment: this beam's own keys, folded into the same state
-    const size_t sbase = (((size_t)r * W + beam) * Ls_cap * nkv + g) * D;
-    for (int j = 0; j < Ls; ++j) {
-        const uint16_t *krow = sk + sbase + (size_t)j * row_stride;
-        const uint16_t *vrow = sv + sbase + (size_t)j * row_stride;
-        float part = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 kv = {0u, 0u, 0u, 0u};
-            if (row_valid) kv = *(const u32x4 *)(krow + ks * 16 + half * 8);
-            const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(kv[e]), part);
-                part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(kv[e]), part);
-            }
-        }
-        const float s = pair_sum(part);
-        const float m_new = fmaxf(st.m, s);
-        const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);
-        const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
-        st.l = st.l * alpha + (half == 0 ? p : 0.f);
-        st.m = m_new;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int rgi = 0; rgi < 4; ++rgi) {
-                u32x2 vv = {0u, 0u};
-                if (row_valid) vv = *(const u32x2 *)(vrow + b * 32 + rgi * 8 + half * 4);
-                st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
-                st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
-                st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
-                st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
-            }
-    }
+    suffix();
+    bool row_valid;
+    int beam;
+    const size_t qrow_idx = query_row(row_valid, beam);
     st.finish(out + qrow_idx * D, lse ? lse + qrow_idx : nullptr, row_valid, scale);
 }
 

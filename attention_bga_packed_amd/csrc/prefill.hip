@@ -8,14 +8,14 @@
 // softmax.
 //
 // Work unit = (kv head g, sequence, query tile of BM = 32*TS tokens). The
-// workgroup holds H*TS waves (H = the group's G query heads, split in halves
-// when G > 8): wave w serves one query head for the 32 tokens of sub-tile w / H,
-// so every K/V tile staged in LDS is shared by H query heads and TS sub-tiles. Keys run from the start of
-// the sequence to the end of the query tile; only tiles that reach past a
-// wave's first query are masked, and tiles entirely after a wave's last query
-// are skipped by that wave.
+// workgroup holds H*TS waves (H = up to 8 of the group's G query heads at
+// d 128, up to 4 at d 64; larger groups are split over several workgroups):
+// wave w serves one query head for the 32 tokens of sub-tile w / H, so every
+// K/V tile staged in LDS is shared by H query heads and TS sub-tiles. Keys run
+// from the start of the sequence to the end of the query tile; only tiles
+// that reach past a wave's first query are masked.
 //
-// Grid = (Nkv, B, max tiles per sequence). The tile index is reversed so the
+// Grid = (Nkv * splits, B, max tiles per sequence). The tile index is reversed so the
 // longest (last) query tiles of every sequence are dispatched first. With
 // consecutive workgroups dealt round-robin over the 8 XCDs, putting the kv head
 // in x keeps all tiles of one (sequence, kv head) on the same XCD (and L2)
@@ -25,8 +25,9 @@
 
 namespace bga {
 
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void packed_prefill_kernel(
+// NW: waves per workgroup when fixed at compile time (0: any)
+template <int D, int NW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void packed_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, int nq, int nkv, int group, int hsplit, int hpw, int ts_per_wg, float scale,
     uint16_t *__restrict__ out, float *__restrict__ lse)
@@ -61,8 +62,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
     st.init(lds);
     const float c2 = scale * kLog2e;
     const uint32_t row_stride = (uint32_t)(nkv * D);
-    DmaPlan<D> plan;
-    plan.init(w, nthr >> 6, row_stride);
+    DmaPlan<D, NW> plan;
+    plan.init(w, nthr >> 6);
     // tile kt needs masking when it reaches past this wave's first query; tiles
     // entirely after the wave's last query are fully masked (contribute zero)
     auto need_mask = [&](int kt) { return s0 + kt * AttnTile<D>::BN + AttnTile<D>::BN - 1 > qw0; };
@@ -79,18 +80,32 @@ static hipError_t launch_prefill_d(const uint16_t *q, const uint16_t *k, const u
                                    float *lse, hipStream_t stream)
 {
     const int group = nq / nkv;
-    const int hsplit = (group + 7) / 8;              // <= 8 query heads per workgroup
+    // At d 64 a wave fits in 168 registers (3 waves per SIMD, 12 per CU): groups are
+    // split into workgroups of <= 4 query heads so that several workgroups share a
+    // CU and one's prologue and epilogue overlap another's tiles. At d 128 (2 waves
+    // per SIMD) up to 8 heads share a workgroup.
+    const int hsplit = D == 64 ? (group + 3) / 4 : (group + 7) / 8;
     const int hpw = (group + hsplit - 1) / hsplit;
     const int ts = hpw >= 4 ? 1 : (hpw == 1 ? 4 : 2); // >= 4 waves per workgroup
     const int bm = 32 * ts;
     const int tiles = (max_seqlen + bm - 1) / bm;
+    const int nw = hpw * ts;
+    const void *kern = nw == 4   ? (const void *)packed_prefill_kernel<D, 4>
+                       : nw == 8 ? (const void *)packed_prefill_kernel<D, 8>
+                                 : (const void *)packed_prefill_kernel<D, 0>;
     const size_t smem = AttnTile<D>::SMEM_BYTES;
-    hipError_t e = hipFuncSetAttribute((const void *)packed_prefill_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    dim3 grid(nkv * hsplit, num_seqs, tiles), block(64 * hpw * ts);
-    hipLaunchKernelGGL(packed_prefill_kernel<D>, grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit, hpw,
-                       ts, scale, out, lse);
+    dim3 grid(nkv * hsplit, num_seqs, tiles), block(64 * nw);
+    if (nw == 4)
+        hipLaunchKernelGGL((packed_prefill_kernel<D, 4>), grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit,
+                           hpw, ts, scale, out, lse);
+    else if (nw == 8)
+        hipLaunchKernelGGL((packed_prefill_kernel<D, 8>), grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit,
+                           hpw, ts, scale, out, lse);
+    else
+        hipLaunchKernelGGL((packed_prefill_kernel<D, 0>), grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit,
+                           hpw, ts, scale, out, lse);
     return hipGetLastError();
 }
 
