@@ -29,7 +29,8 @@ HIPCC_FLAGS = [
 # The attention kernels never produce or consume NaN on purpose (masking uses
 # -inf); letting the compiler drop IEEE NaN quieting turns max chains into v_max3.
 PER_FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-                  "decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+                  "decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+                  "topk.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def sources():

@@ -13,19 +13,23 @@
 // +0); key 0 is the NaN pattern 0xffff and marks "no element". An fp32 score
 // maps to a 32-bit key the same way.
 //
-// Stage 1 (one 256-thread workgroup per beam row, several per CU):
-//   pass 1 streams the row from HBM once. Each wave keeps its running maximum
-//   key M_w, an fp64 sum of exp(x - M_w) per lane (fp32 exponentials, rescaled
-//   when M_w grows) and an exact histogram of the 256 keys [M_w - 255, M_w]
-//   (shifted when M_w grows; keys below the window can never re-enter it).
-//   The waves' windows merge exactly into the histogram of [M - 255, M], M the
-//   row maximum, from which the cut key kappa (the k-th largest) and the number
-//   of keys above it follow directly. If the window holds fewer than k keys a
-//   generic two-digit radix select over the row is used instead.
-//   pass 2 re-reads the row (from cache) and gathers every key >= kappa; a
-//   bitonic sort by (key desc, id asc) then puts the k winners first, which
-//   also breaks ties at kappa by lower id. If too many keys equal kappa to fit,
-//   ties are ranked by id with a block scan in id order instead.
+// Stage 1 (one 256-thread workgroup per beam row, several per CU) reads the
+// row from HBM once:
+//   threshold: the keys of an evenly strided sample of 4096 logits give a
+//     cut t whose expected count in the row is about 2.5k (k = k_local); for
+//     rows that fit the candidate list whole, t takes every element.
+//   stream: every lane keeps a running offset m (its largest logit so far,
+//     moved lazily) and an fp64 sum of fp32 exp(x - m); elements with key >= t
+//     are appended to an LDS candidate list (a lane first checks its chunk
+//     maximum against t, so the append path is rare).
+//   selection: if the list holds at least k keys (and did not overflow), the
+//     k-th largest key of the row is the k-th largest of the list, found by an
+//     exact radix select; the entries at or above it are sorted by
+//     (key desc, id asc), which also breaks ties by lower id. Otherwise (a
+//     sample far from the row's distribution) the row is read again and the
+//     cut found by a radix select over the whole row; if too many keys equal
+//     the cut to sort, ties are ranked by id with a block scan in id order.
+//   The lanes' (m, sum) pairs merge into the row's fp32 log-sum-exp.
 // Stage 2 (one workgroup per request): each beam's list is sorted, so only its
 // first min(k_local, k_global) entries can matter and the entries above any
 // threshold form a prefix. A lower bound comes from the first J entries of
@@ -37,11 +41,15 @@
 
 namespace bga {
 
+struct Parity0 { static constexpr int value = 0; };
+struct Parity1 { static constexpr int value = 1; };
+
 constexpr int TK1_THREADS = 256;   // stage 1: one workgroup per beam row
 constexpr int TK1_WAVES = TK1_THREADS / 64;
 constexpr int TK1_UNROLL = 4;      // 16-byte chunks in flight per thread
-constexpr int TK_WIN = 256;        // keys per histogram window
-constexpr int TK_LIST = 2048;      // gathered candidates (>= k + ties)
+constexpr int TK_LIST = 4096;      // candidate list entries
+constexpr int TK_SAMPLE = 512;     // sampled 8-logit chunks (4096 logits)
+constexpr int TK_WCHUNKS = 1024;   // per wave: chunks with a candidate (stream)
 constexpr int TK2_THREADS = 1024;  // stage 2: one workgroup per request, one beam per thread
 
 __device__ __forceinline__ uint32_t key16(uint32_t b)
@@ -171,6 +179,125 @@ __device__ __forceinline__ void bitonic_desc(unsigned long long *list, int n)
     }
 }
 
+// Bitonic sort of list[0..1024) into descending order by 256 threads. Each
+// thread holds the elements at positions tid + 256 i (i < 4): exchanges at
+// distance 256 and 512 stay in the thread, distances below 64 are lane
+// shuffles within the wave, and only distances 64 and 128 go through LDS.
+__device__ __forceinline__ void bitonic1024_desc(unsigned long long *list)
+{
+    const int tid = threadIdx.x;
+    unsigned long long v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = list[tid + 256 * i];
+    auto cas = [](unsigned long long &a, unsigned long long &b, bool desc) {   // a at the lower position
+        const bool swap = desc ? (a < b) : (a > b);
+        const unsigned long long lo = swap ? b : a, hi = swap ? a : b;
+        a = lo;
+        b = hi;
+    };
+#pragma unroll 1
+    for (int size = 2; size <= 1024; size <<= 1) {
+#pragma unroll 1
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 256) {
+                const int d = stride / 256;   // 1 or 2
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!(i & d)) cas(v[i], v[i | d], ((tid + 256 * i) & size) == 0);
+            } else if (stride >= 64) {
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) list[tid + 256 * i] = v[i];
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = tid + 256 * i;
+                    const unsigned long long o = list[pos ^ stride];
+                    const bool lower = (pos & stride) == 0, desc = (pos & size) == 0;
+                    const bool take_max = lower == desc;
+                    v[i] = take_max ? (v[i] > o ? v[i] : o) : (v[i] < o ? v[i] : o);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = tid + 256 * i;
+                    const uint32_t lo = __shfl_xor((uint32_t)v[i], stride), hi = __shfl_xor((uint32_t)(v[i] >> 32), stride);
+                    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+                    const bool lower = (pos & stride) == 0, desc = (pos & size) == 0;
+                    const bool take_max = lower == desc;
+                    v[i] = take_max ? (v[i] > o ? v[i] : o) : (v[i] < o ? v[i] : o);
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) list[tid + 256 * i] = v[i];
+    __syncthreads();
+}
+
+// Value held by lane (lane ^ stride) of the wave, stride a power of two < 64:
+// DPP quad permutes for 1 and 2, LDS-free swizzles for 4..16, a row swap for 32.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int stride)
+{
+    switch (stride) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (4 << 10));
+    case 8: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (8 << 10));
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (16 << 10));
+    default: {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? p[0] : p[1];
+    }
+    }
+}
+
+// Bitonic sort into descending order of 1024 32-bit values held 4 per thread
+// by 256 threads (v[i] at position tid + 256 i). Distances 256 and 512 stay
+// in the thread, distances below 64 are lane exchanges, 64 and 128 go through
+// `scratch` (1024 words of LDS).
+__device__ __forceinline__ void bitonic1024_desc_u32(uint32_t (&v)[4], uint32_t *scratch)
+{
+    const int tid = threadIdx.x;
+#pragma unroll 1
+    for (int size = 2; size <= 1024; size <<= 1) {
+#pragma unroll 1
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 256) {
+                const int d = stride / 256;   // 1 or 2
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!(i & d)) {
+                        const bool desc = ((tid + 256 * i) & size) == 0;
+                        const uint32_t a = v[i], b = v[i | d];
+                        v[i] = desc ? max(a, b) : min(a, b);
+                        v[i | d] = desc ? min(a, b) : max(a, b);
+                    }
+            } else {
+                uint32_t o[4];
+                if (stride >= 64) {
+                    __syncthreads();
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) scratch[tid + 256 * i] = v[i];
+                    __syncthreads();
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = scratch[(tid + 256 * i) ^ stride];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = lane_xor(v[i], stride);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = tid + 256 * i;
+                    const bool take_max = ((pos & stride) == 0) == ((pos & size) == 0);
+                    v[i] = take_max ? max(v[i], o[i]) : min(v[i], o[i]);
+                }
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ int pow2_at_least(int n)
 {
     int p = 1;
@@ -182,34 +309,85 @@ __device__ __forceinline__ int pow2_at_least(int n)
 
 struct Tk1Shared {
     TkCommon c;
-    uint32_t whist[TK1_WAVES][TK_WIN];   // per-wave window histograms
-    uint32_t wmax[TK1_WAVES];
-    double dsum[TK1_WAVES];
-    unsigned long long list[TK_LIST];
+    union {
+        unsigned long long list[TK_LIST];     // candidates: key << 32 | ~id
+        uint16_t sample[TK_SAMPLE * 8];       // sampled keys (before the stream)
+        int32_t chunks[TK1_THREADS / 64][TK_WCHUNKS];   // per wave: chunks holding keys >= t (stream)
+    };
+    uint32_t whist[TK1_THREADS / 64][256];    // per-wave digit histograms of the sample
+    float lmax[TK1_THREADS / 64];
+    double dsum[TK1_THREADS / 64];
+    uint32_t wcnt[TK1_THREADS / 64];
     uint32_t count;
 };
 
-// Row chunk c (8 logits, ids 8c .. 8c+7) as four packed key pairs; missing
-// logits get key 0.
+// The j-th largest nonzero key of sh.sample[0..n) (two 8-bit digits; each wave
+// counts into its own histogram, since sample keys crowd into a few digits).
+__device__ __forceinline__ uint32_t sample_select(Tk1Shared &sh, int n, uint32_t j)
+{
+    const int tid = threadIdx.x, w = tid >> 6;
+    uint32_t prefix = 0, mask = 0, krem = j;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = 8 * (1 - pass);
+        for (int i = tid; i < (TK1_THREADS / 64) * 256; i += TK1_THREADS) (&sh.whist[0][0])[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += TK1_THREADS) {
+            const uint32_t key = sh.sample[i];
+            if (key && (key & mask) == prefix) atomicAdd(&sh.whist[w][(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < TK1_THREADS / 64; ++i) c += sh.whist[i][tid];
+            sh.c.hist[tid] = c;
+        }
+        __syncthreads();
+        select_bin(sh.c, sh.c.hist, krem);
+        krem -= sh.c.bcast[1];
+        prefix |= sh.c.bcast[0] << shift;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// Raw bf16 bits of row chunk c (8 logits, ids 8c .. 8c+7) as four packed pairs;
+// logits beyond the row read as -inf (0xff80). The load itself is clamped to
+// the row and never skipped, so that a wave's loads are issued unconditionally
+// (the compiler can then wait for exactly the loads it needs).
+template <bool VEC>
+__device__ __forceinline__ u32x4 load_raw(const uint16_t *__restrict__ x, int c, int V, int nchunks)
+{
+    u32x4 raw;
+    if (VEC) {
+        raw = *(const u32x4 *)(x + (size_t)min(c, nchunks - 1) * 8);
+        if (c >= nchunks) raw = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const int id = c * 8 + j;
+            const uint32_t b0 = x[min(id, V - 1)], b1 = x[min(id + 1, V - 1)];
+            raw[j / 2] = (id < V ? b0 : 0xff80u) | ((id + 1 < V ? b1 : 0xff80u) << 16);
+        }
+    }
+    return raw;
+}
+
+// Keys of a chunk; logits beyond the row get key 0 (no element).
 template <bool VEC>
 __device__ __forceinline__ u32x4 load_keys(const uint16_t *__restrict__ x, int c, int V, int nchunks)
 {
-    u32x4 raw = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-    if (c < nchunks) {
-        if (VEC) {
-            raw = *(const u32x4 *)(x + (size_t)c * 8);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int id = c * 8 + j;
-                const uint32_t b = id < V ? (uint32_t)x[id] : 0xffffu;
-                raw[j / 2] = (j & 1) ? ((raw[j / 2] & 0xffffu) | (b << 16)) : ((raw[j / 2] & 0xffff0000u) | b);
-            }
-        }
-    }
+    const u32x4 raw = load_raw<VEC>(x, c, V, nchunks);
     u32x4 k;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k[e] = key16(raw[e] & 0xffffu) | (key16(raw[e] >> 16) << 16);
+    for (int e = 0; e < 4; ++e) {
+        const int id = c * 8 + 2 * e;
+        const uint32_t lo = id < V ? key16(raw[e] & 0xffffu) : 0u;
+        const uint32_t hi = id + 1 < V ? key16(raw[e] >> 16) : 0u;
+        k[e] = lo | (hi << 16);
+    }
     return k;
 }
 
@@ -230,99 +408,301 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     const int nrows = (nchunks + TK1_THREADS - 1) / TK1_THREADS;   // chunk rows, id order
     const uint32_t k = (uint32_t)k_local;
 
-    for (int i = lane; i < TK_WIN; i += 64) sh.whist[w][i] = 0;
+    // the stream's first chunks go out now: they land while the threshold is chosen
+    u32x4 bufa[TK1_UNROLL], bufb[TK1_UNROLL];
+#pragma unroll
+    for (int u = 0; u < TK1_UNROLL; ++u) bufa[u] = load_raw<VEC>(x, u * TK1_THREADS + tid, V, nchunks);
 
-    // ---- pass 1: running max, log-sum-exp and window histogram, per wave
-    uint32_t mw = 0;          // wave running max key (0: nothing seen yet)
-    float mwv = 0.f;          // its value
-    double acc = 0.0;         // sum of exp(x - mwv) over this lane's logits
-    uint32_t *hist = sh.whist[w];
-    for (int i0 = 0; i0 < nrows; i0 += TK1_UNROLL) {
-        u32x4 kk[TK1_UNROLL];
+    // ---- threshold key t from a strided sample (t = 1: every element)
+    uint32_t tkey = 1u;
+    if (V > TK_LIST) {
+        const int ns = min(nchunks, TK_SAMPLE);
+        for (int i = tid; i < ns; i += TK1_THREADS) {
+            const int c = (int)(((long long)i * nchunks) / ns);
+            const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
 #pragma unroll
-        for (int u = 0; u < TK1_UNROLL; ++u) kk[u] = load_keys<VEC>(x, (i0 + u) * TK1_THREADS + tid, V, nchunks);
-        uint32_t lm = 0;
-#pragma unroll
-        for (int u = 0; u < TK1_UNROLL; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) lm = max(lm, max(kk[u][e] & 0xffffu, kk[u][e] >> 16));
-        const uint32_t nm = wave_max_u32(lm);
-        if (nm > mw) {  // wave-uniform
-            const float nmv = key16_value(nm);
-            if (mw != 0) acc *= exp((double)mwv - (double)nmv);
-            // shift the window so that it ends at the new maximum
-            const uint32_t d = nm - mw;
-            uint32_t vals[TK_WIN / 64];
-#pragma unroll
-            for (int j = 0; j < TK_WIN / 64; ++j) {
-                const uint32_t src = (uint32_t)(lane * (TK_WIN / 64) + j) + d;
-                vals[j] = (mw != 0 && src < TK_WIN) ? hist[src] : 0u;
+            for (int e = 0; e < 4; ++e) {
+                sh.sample[i * 8 + 2 * e] = (uint16_t)(kk[e] & 0xffffu);
+                sh.sample[i * 8 + 2 * e + 1] = (uint16_t)(kk[e] >> 16);
             }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int j = 0; j < TK_WIN / 64; ++j) hist[lane * (TK_WIN / 64) + j] = vals[j];
-            __builtin_amdgcn_wave_barrier();
-            mw = nm;
-            mwv = nmv;
         }
-        const uint32_t base = mw > TK_WIN - 1 ? mw - (TK_WIN - 1) : 1u;
-        const float mlog = mwv * kLog2e;
+        __syncthreads();
+        const int nsamp = ns * 8;
+        // expected count of row keys >= the j-th largest sample key: about j * V / nsamp = 2.5k
+        const uint32_t j = (uint32_t)min((long long)nsamp, (5ll * k * nsamp + 2ll * V - 1) / (2ll * V) + 8);
+        tkey = sample_select(sh, nsamp, j);
+        __syncthreads();   // the sample is dead: the list reuses its memory
+    }
+    const float tval = tkey > 1u ? key16_value(tkey) : -INFINITY;   // value form of the cut (prefilter)
+    __syncthreads();
+
+    // ---- stream: per-lane lazy offset m and fp64 sum of exp(x - m); note chunks with keys >= t
+    float m = -INFINITY;
+    double acc = 0.0;
+    uint32_t wcount = 0;   // chunks this wave noted (wave-uniform)
+    // two buffers of chunks: one is reduced while the other is in flight
+    auto load_batch = [&](u32x4 (&buf)[TK1_UNROLL], int i0) {
+#pragma unroll
+        for (int u = 0; u < TK1_UNROLL; ++u) buf[u] = load_raw<VEC>(x, (i0 + u) * TK1_THREADS + tid, V, nchunks);
+    };
+    auto consume = [&](const u32x4 (&raw)[TK1_UNROLL], int i0) {
+        float cmax[TK1_UNROLL];
 #pragma unroll
         for (int u = 0; u < TK1_UNROLL; ++u) {
+            float c = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c = fmaxf(c, fmaxf(bf16_lo(raw[u][e]), bf16_hi(raw[u][e])));
+            cmax[u] = c;
+        }
+        float lm = cmax[0];
+#pragma unroll
+        for (int u = 1; u < TK1_UNROLL; ++u) lm = fmaxf(lm, cmax[u]);
+        if (lm > m + 8.f) {   // lazy: exp(x - m) stays <= e^8 between moves
+            if (m != -INFINITY) acc *= (double)__builtin_amdgcn_exp2f((m - lm) * kLog2e);
+            m = lm;
+        }
+        if (m != -INFINITY) {
+            const float mlog = m * kLog2e;
             float cs = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int u = 0; u < TK1_UNROLL; ++u)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t key = (kk[u][e] >> (16 * h)) & 0xffffu;
-                    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(key16_value(key), kLog2e, -mlog));
-                    cs += key ? t : 0.f;
-                    if (key >= base) atomicAdd(&hist[key - base], 1u);
+                for (int e = 0; e < 4; ++e) {
+                    cs += __builtin_amdgcn_exp2f(__builtin_fmaf(bf16_lo(raw[u][e]), kLog2e, -mlog));
+                    cs += __builtin_amdgcn_exp2f(__builtin_fmaf(bf16_hi(raw[u][e]), kLog2e, -mlog));
                 }
             acc += (double)cs;
         }
+#pragma unroll
+        for (int u = 0; u < TK1_UNROLL; ++u) {   // note the chunks that hold keys >= t
+            const bool hit = cmax[u] >= tval;
+            const unsigned long long mask = __ballot(hit);
+            if (mask) {   // wave-uniform; the wave's own region, no atomics
+                const uint32_t pos = wcount + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (hit && pos < (uint32_t)TK_WCHUNKS) sh.chunks[w][pos] = (i0 + u) * TK1_THREADS + tid;
+                wcount += (uint32_t)__popcll(mask);
+            }
+        }
+    };
+    for (int i0 = 0; i0 < nrows; i0 += 2 * TK1_UNROLL) {
+        load_batch(bufb, i0 + TK1_UNROLL);
+        consume(bufa, i0);
+        load_batch(bufa, i0 + 2 * TK1_UNROLL);
+        consume(bufb, i0 + TK1_UNROLL);
     }
 
-    // ---- merge the waves: row max, log-sum-exp, window histogram of [M-255, M]
-    if (lane == 0) sh.wmax[w] = mw;
+    // ---- candidates: the keys >= t of the noted chunks (read again, from cache)
+    if (lane == 0) sh.wcnt[w] = wcount;
     __syncthreads();
-    uint32_t M = 0;
+    uint32_t wc[TK1_THREADS / 64], wtot = 0;
+    bool noted_all = true;
 #pragma unroll
-    for (int i = 0; i < TK1_WAVES; ++i) M = max(M, sh.wmax[i]);
-    const float Mv = key16_value(M);
-    acc = wave_sum_f64(acc);
-    if (lane == 0) sh.dsum[w] = (mw != 0) ? acc * exp((double)mwv - (double)Mv) : 0.0;
-    const uint32_t gbase = M > TK_WIN - 1 ? M - (TK_WIN - 1) : 1u;
-    for (int b = tid; b < TK_WIN; b += TK1_THREADS) {
-        uint32_t s = 0;
-        const uint32_t key = gbase + b;
-#pragma unroll
-        for (int i = 0; i < TK1_WAVES; ++i) {
-            const uint32_t mwi = sh.wmax[i];
-            const uint32_t bi = mwi > TK_WIN - 1 ? mwi - (TK_WIN - 1) : 1u;
-            if (mwi != 0 && key >= bi && key <= mwi) s += sh.whist[i][key - bi];
-        }
-        sh.c.hist[b] = s;
+    for (int i = 0; i < TK1_THREADS / 64; ++i) {
+        wc[i] = sh.wcnt[i];
+        noted_all = noted_all && wc[i] <= (uint32_t)TK_WCHUNKS;
+        wc[i] = min(wc[i], (uint32_t)TK_WCHUNKS);
+        wtot += wc[i];
     }
+    constexpr int kPer = TK1_WAVES * TK_WCHUNKS / TK1_THREADS;   // noted chunks per thread, at most
+    int mych[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        // flat index over the waves' regions
+        uint32_t f = (uint32_t)(tid + j * TK1_THREADS), c = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < TK1_THREADS / 64; ++i) {
+            if (c == 0xffffffffu && f < wc[i]) c = (uint32_t)sh.chunks[i][f];
+            f = f >= wc[i] ? f - wc[i] : 0xffffffffu;
+        }
+        mych[j] = (int)c;
+    }
+    __syncthreads();   // the chunk lists are read: the candidate list takes their memory
+    // The noted chunks in two rounds of 8 per thread: a round's chunks are all in
+    // flight at once (empty slots read chunk 0), candidates are counted, and one
+    // block scan places them (no atomics).
+    uint32_t at_total = 0;
+    auto gather_round = [&](auto round) {
+        constexpr int r = decltype(round)::value;
+        u32x4 craw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) craw[j] = load_raw<VEC>(x, max(mych[r * 8 + j], 0), V, nchunks);
+        uint32_t hits[8], ncand = 0;   // per chunk: bit e*2+h set for a candidate
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = mych[r * 8 + j];
+            uint32_t hm = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hm |= (bf16_lo(craw[j][e]) >= tval ? 1u : 0u) << (2 * e);
+                hm |= (bf16_hi(craw[j][e]) >= tval ? 1u : 0u) << (2 * e + 1);
+            }
+            // finite logits: value order is key order; drop empty slots and ids >= V
+            const int valid = c < 0 ? 0 : min(8, V - c * 8);
+            hm &= (1u << valid) - 1u;
+            hits[j] = hm;
+            ncand += (uint32_t)__popc(hm);
+        }
+        uint32_t rtotal;
+        uint32_t at = at_total + block_excl_scan(sh.c, ncand, &rtotal);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t hm = hits[j];
+            while (hm) {
+                const int b = __ffs(hm) - 1;
+                hm &= hm - 1;
+                const uint32_t word = craw[j][b >> 1];
+                const uint32_t key = key16((b & 1) ? (word >> 16) : (word & 0xffffu));
+                const uint32_t id = (uint32_t)(mych[r * 8 + j] * 8 + b);
+                if (at < (uint32_t)TK_LIST) sh.list[at] = ((unsigned long long)key << 32) | (0xffffffffu - id);
+                ++at;
+            }
+        }
+        at_total += rtotal;
+    };
+    static_assert(kPer == 16, "two gather rounds of 8 chunks per thread");
+    gather_round(Parity0{});
+    if (wtot > (uint32_t)(8 * TK1_THREADS)) gather_round(Parity1{});   // uniform
+    if (tid == 0) sh.count = at_total;
+    __syncthreads();
+
+    // ---- the row's log-sum-exp from the lanes' (m, sum)
+    float M = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) sh.lmax[w] = M;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TK1_THREADS / 64; ++i) M = fmaxf(M, sh.lmax[i]);
+    double part = (m != -INFINITY) ? acc * exp((double)m - (double)M) : 0.0;
+    part = wave_sum_f64(part);
+    if (lane == 0) sh.dsum[w] = part;
     __syncthreads();
     double tot = 0.0;
 #pragma unroll
-    for (int i = 0; i < TK1_WAVES; ++i) tot += sh.dsum[i];
-    const float lse32 = (float)((double)Mv + log(tot));
+    for (int i = 0; i < TK1_THREADS / 64; ++i) tot += sh.dsum[i];
+    const float lse32 = (float)((double)M + log(tot));
 
-    uint32_t in_win = 0;
-    for (int b = 0; b < TK_WIN; ++b) in_win += sh.c.hist[b];   // uniform, LDS broadcast reads
+    const float c0 = cum ? cum[row] : 0.f;
+    auto emit = [&](int j, uint32_t key, int32_t id) {
+        const float lp = key16_value(key) - lse32;
+        const float s = c0 + lp;
+        const size_t o = row * (size_t)k_local + j;
+        ws_tok[o] = id;
+        ws_score[o] = s;
+        if (local_tok) local_tok[o] = id;
+        if (local_score) local_score[o] = s;
+    };
 
     // ---- the cut key kappa, keys above it, keys equal to it
+    const uint32_t count = sh.count;
     uint32_t kappa, above, n_eq;
-    if (in_win >= k) {
-        select_bin(sh.c, sh.c.hist, k);
-        kappa = gbase + sh.c.bcast[0];
-        above = sh.c.bcast[1];
-        n_eq = sh.c.bcast[2];
+    int n;
+    if (noted_all && count >= k && count <= (uint32_t)TK_LIST) {
+        // Common case: a counting sort by key offset from t. Every listed key
+        // is >= t; when they span < 1024 values, bins give each key's place
+        // (keys above it) and ranks by id inside a bin finish the order.
+        constexpr int kPerT = TK_LIST / TK1_THREADS;
+        unsigned long long ent[kPerT];
+        bool wide = false;
+#pragma unroll
+        for (int j = 0; j < kPerT; ++j) {
+            const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
+            ent[j] = idx < count ? sh.list[idx] : 0ull;
+            wide = wide || (idx < count && (uint32_t)(ent[j] >> 32) - tkey >= 1024u);
+        }
+        if (!__syncthreads_or(wide)) {
+            uint32_t *hist = &sh.whist[0][0];                     // 1024 bins
+            uint32_t *start = (uint32_t *)sh.list;                 // keys above each bin
+            unsigned long long *bkt = sh.list + 512;               // selected entries, bin by bin
+            for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kPerT; ++j)
+                if ((uint32_t)(tid + j * TK1_THREADS) < count) atomicAdd(&hist[(uint32_t)(ent[j] >> 32) - tkey], 1u);
+            __syncthreads();
+            uint32_t hc[4], loc = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                hc[q] = hist[1023 - 4 * tid - q];   // thread t: bins 1023-4t down to 1020-4t
+                loc += hc[q];
+            }
+            if (tid == 0) sh.c.bcast[1] = 0;
+            uint32_t tot;
+            uint32_t run = block_excl_scan(sh.c, loc, &tot);   // (the list is in registers: its memory is free)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int b = 1023 - 4 * tid - q;
+                start[b] = run;
+                if (run < k && run + hc[q] >= k) sh.c.bcast[0] = (uint32_t)b;
+                run += hc[q];
+            }
+            __syncthreads();
+            const uint32_t bk = sh.c.bcast[0];   // bin of the k-th largest key
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if ((uint32_t)(1023 - 4 * tid - q) >= bk) atomicMax(&sh.c.bcast[1], hc[q]);
+            __syncthreads();
+            const uint32_t nsel = start[bk] + hist[bk], bmax = sh.c.bcast[1];
+            __syncthreads();   // every thread has read nsel and bmax: the decision is uniform
+            if (nsel <= 1024 && bmax <= 64) {
+                for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;   // now: fill cursors
+                __syncthreads();
+                uint32_t pos[kPerT];
+#pragma unroll
+                for (int j = 0; j < kPerT; ++j) {
+                    const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey;
+                    pos[j] = 0xffffffffu;
+                    if ((uint32_t)(tid + j * TK1_THREADS) < count && dk >= bk) {
+                        const uint32_t b0 = start[dk];
+                        pos[j] = b0;
+                        bkt[b0 + atomicAdd(&hist[dk], 1u)] = ent[j];
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < kPerT; ++j)
+                    if (pos[j] != 0xffffffffu) {
+                        const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey, nb = hist[dk];
+                        const uint32_t myid = 0xffffffffu - (uint32_t)(ent[j] & 0xffffffffu);
+                        uint32_t rank = 0;
+                        for (uint32_t i = 0; i < nb; ++i)
+                            rank += (0xffffffffu - (uint32_t)(bkt[pos[j] + i] & 0xffffffffu)) < myid;
+                        const uint32_t at = pos[j] + rank;
+                        if (at < (uint32_t)k_local) emit((int)at, tkey + dk, (int32_t)myid);
+                    }
+                if (tid == 0 && row_lse) row_lse[row] = lse32;
+                return;
+            }
+            // put the list back for the general path below
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kPerT; ++j) {
+                const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
+                if (idx < count) sh.list[idx] = ent[j];
+            }
+            __syncthreads();
+        }
+        // every row key >= t is listed, and the k-th largest is one of them
+        kappa = radix_select<2>(sh.c, [&](auto fn) {
+            for (uint32_t i = tid; i < count; i += TK1_THREADS) fn((uint32_t)(sh.list[i] >> 32));
+        }, k, &above, &n_eq);
+        // keep the entries >= kappa (order does not matter: they are sorted next)
+        unsigned long long mine[TK_LIST / TK1_THREADS];
+#pragma unroll
+        for (int i = 0; i < TK_LIST / TK1_THREADS; ++i) {
+            const uint32_t idx = (uint32_t)(tid + i * TK1_THREADS);
+            mine[i] = idx < count ? sh.list[idx] : 0ull;
+        }
         __syncthreads();
+        if (tid == 0) sh.count = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TK_LIST / TK1_THREADS; ++i)
+            if ((uint32_t)(mine[i] >> 32) >= kappa) sh.list[atomicAdd(&sh.count, 1u)] = mine[i];
+        n = (int)(above + n_eq);
     } else {
-        // generic path: two 8-bit digits over the whole row
+        // the sample misled the threshold: cut by a radix select over the whole row
         kappa = radix_select<2>(sh.c, [&](auto fn) {
             for (int i = 0; i < nrows; ++i) {
                 const u32x4 kk = load_keys<VEC>(x, i * TK1_THREADS + tid, V, nchunks);
@@ -333,76 +713,94 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
                 }
             }
         }, k, &above, &n_eq);
-    }
-    const uint32_t need = k - above;   // keys equal to kappa that are kept (1 <= need <= n_eq)
-
-    // ---- pass 2: gather the winners
-    if (tid == 0) sh.count = 0;
-    __syncthreads();
-    int n;
-    if (above + n_eq <= (uint32_t)TK_LIST) {
-        // every key >= kappa; the sort puts ties in id order
-        for (int i = 0; i < nrows; ++i) {
-            const int c = i * TK1_THREADS + tid;
-            const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
+        const uint32_t need = k - above;   // keys equal to kappa that are kept (1 <= need <= n_eq)
+        if (tid == 0) sh.count = 0;
+        __syncthreads();
+        if (above + n_eq <= (uint32_t)TK_LIST) {
+            // every key >= kappa; the sort puts ties in id order
+            for (int i = 0; i < nrows; ++i) {
+                const int c = i * TK1_THREADS + tid;
+                const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t key = (kk[e] >> (16 * h)) & 0xffffu;
-                    if (key >= kappa && key != 0) {
-                        const uint32_t slot = atomicAdd(&sh.count, 1u);
-                        sh.list[slot] = ((unsigned long long)key << 32) | (0xffffffffu - (uint32_t)(c * 8 + e * 2 + h));
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t key = (kk[e] >> (16 * h)) & 0xffffu;
+                        if (key >= kappa && key != 0) {
+                            const uint32_t slot = atomicAdd(&sh.count, 1u);
+                            sh.list[slot] = ((unsigned long long)key << 32) | (0xffffffffu - (uint32_t)(c * 8 + e * 2 + h));
+                        }
                     }
-                }
-        }
-        n = (int)(above + n_eq);
-    } else {
-        // too many ties to hold: rank them by id, row of chunks by row of chunks
-        uint32_t run = 0;
-        for (int i = 0; i < nrows; ++i) {
-            const int c = i * TK1_THREADS + tid;
-            const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
-            uint32_t nt = 0;
+            }
+            n = (int)(above + n_eq);
+        } else {
+            // too many ties to hold: rank them by id, row of chunks by row of chunks
+            uint32_t run = 0;
+            for (int i = 0; i < nrows; ++i) {
+                const int c = i * TK1_THREADS + tid;
+                const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
+                uint32_t nt = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) nt += ((kk[e] & 0xffffu) == kappa) + ((kk[e] >> 16) == kappa);
-            uint32_t rowtot;
-            uint32_t rank = run + block_excl_scan(sh.c, nt, &rowtot);
+                for (int e = 0; e < 4; ++e) nt += ((kk[e] & 0xffffu) == kappa) + ((kk[e] >> 16) == kappa);
+                uint32_t rowtot;
+                uint32_t rank = run + block_excl_scan(sh.c, nt, &rowtot);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t key = (kk[e] >> (16 * h)) & 0xffffu;
-                    bool take = key > kappa;
-                    if (key == kappa) take = rank++ < need;
-                    if (take) {
-                        const uint32_t slot = atomicAdd(&sh.count, 1u);
-                        sh.list[slot] = ((unsigned long long)key << 32) | (0xffffffffu - (uint32_t)(c * 8 + e * 2 + h));
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t key = (kk[e] >> (16 * h)) & 0xffffu;
+                        bool take = key > kappa;
+                        if (key == kappa) take = rank++ < need;
+                        if (take) {
+                            const uint32_t slot = atomicAdd(&sh.count, 1u);
+                            sh.list[slot] = ((unsigned long long)key << 32) | (0xffffffffu - (uint32_t)(c * 8 + e * 2 + h));
+                        }
                     }
-                }
-            run += rowtot;
+                run += rowtot;
+            }
+            n = (int)k;
         }
-        n = (int)k;
     }
     __syncthreads();
+    if (n <= 1024) {
+        // sort 32-bit words: (key - kappa) << 18 | (2^18 - 1 - id); 0 pads (ids < 2^18 - 1)
+        uint32_t v[4];
+        bool fits = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pos = tid + 256 * i;
+            v[i] = 0u;
+            if (pos < n) {
+                const unsigned long long e = sh.list[pos];
+                const uint32_t dk = (uint32_t)(e >> 32) - kappa;
+                const uint32_t id = 0xffffffffu - (uint32_t)(e & 0xffffffffu);
+                fits = fits && dk < (1u << 14);
+                v[i] = (dk << 18) | (0x3ffffu - id);
+            }
+        }
+        if (__syncthreads_and(fits)) {
+            bitonic1024_desc_u32(v, (uint32_t *)sh.list);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pos = tid + 256 * i;
+                if (pos < k_local) emit(pos, kappa + (v[i] >> 18), (int32_t)(0x3ffffu - (v[i] & 0x3ffffu)));
+            }
+            if (tid == 0 && row_lse) row_lse[row] = lse32;
+            return;
+        }
+    }
     const int width = pow2_at_least(n);
     for (int i = n + tid; i < width; i += TK1_THREADS) sh.list[i] = 0ull;
     __syncthreads();
-    bitonic_desc(sh.list, width);
+    if (width == 1024)
+        bitonic1024_desc(sh.list);
+    else
+        bitonic_desc(sh.list, width);
 
     // ---- scores and outputs
-    const float c0 = cum ? cum[row] : 0.f;
     for (int j = tid; j < k_local; j += TK1_THREADS) {
         const unsigned long long e = sh.list[j];
-        const uint32_t key = (uint32_t)(e >> 32);
-        const int32_t id = (int32_t)(0xffffffffu - (uint32_t)(e & 0xffffffffu));
-        const float lp = key16_value(key) - lse32;
-        const float s = c0 + lp;
-        const size_t o = row * (size_t)k_local + j;
-        ws_tok[o] = id;
-        ws_score[o] = s;
-        if (local_tok) local_tok[o] = id;
-        if (local_score) local_score[o] = s;
+        emit(j, (uint32_t)(e >> 32), (int32_t)(0xffffffffu - (uint32_t)(e & 0xffffffffu)));
     }
     if (tid == 0 && row_lse) row_lse[row] = lse32;
 }
