@@ -43,10 +43,10 @@ KERNEL_SOURCES = {
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
 MEASURED_TRAFFIC = {
-    "packed_gqa_prefill": {"fetch_kib": 18509.2, "write_kib": 19158.1, "sources_sha256": "d5fbe6c590a4a171"},
-    "shared_prefix_decode": {"fetch_kib": 35157.6, "write_kib": 17632.0, "sources_sha256": "dd75cbce1954c050"},
-    "beam_topk": {"fetch_kib": 950790.1, "write_kib": 20037.5, "sources_sha256": "fadf4f07e1cff4bc"},
-    "suffix_reorder": {"fetch_kib": 15208.8, "write_kib": 38400.0, "sources_sha256": "64b133c74e63f310"},
+    "packed_gqa_prefill": {"fetch_kib": 17769.3, "write_kib": 18016.6, "sources_sha256": "e5669ece78ce00ac"},
+    "shared_prefix_decode": {"fetch_kib": 33430.6, "write_kib": 13600.0, "sources_sha256": "b1c0e5cd5586e8fe"},
+    "beam_topk": {"fetch_kib": 862402.1, "write_kib": 26666.9, "sources_sha256": "7ce159611a4e588b"},
+    "suffix_reorder": {"fetch_kib": 15208.7, "write_kib": 38400.0, "sources_sha256": "0626fecf178d2e73"},
 }
 
 
