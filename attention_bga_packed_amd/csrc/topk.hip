@@ -809,9 +809,50 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 
 struct Tk2Shared {
     TkCommon c;
-    unsigned long long list[1024];   // k_global <= 1024
+    unsigned long long list[1024];                 // k_global <= 1024
+    uint32_t whist[TK2_THREADS / 64][256];         // per-wave digit histograms
     uint32_t count;
 };
+
+// Radix select of the k-th largest 32-bit key over the keys `each` visits,
+// with a histogram per wave (scores crowd into a few leading digits).
+// *above = keys strictly greater, *equal = keys equal to the result.
+template <typename Each>
+__device__ __forceinline__ uint32_t radix_select32_w(Tk2Shared &sh, Each each, uint32_t k, uint32_t *above,
+                                                     uint32_t *equal)
+{
+    const int tid = threadIdx.x, w = tid >> 6;
+    constexpr int NW = TK2_THREADS / 64;
+    uint32_t prefix = 0, mask = 0, krem = k, abv = 0, eq = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 8 * (3 - pass);
+        for (int i = tid; i < NW * 256; i += TK2_THREADS) (&sh.whist[0][0])[i] = 0;
+        __syncthreads();
+        each([&](uint32_t key) {
+            if ((key & mask) == prefix) atomicAdd(&sh.whist[w][(key >> shift) & 255u], 1u);
+        });
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) c += sh.whist[i][tid];
+            sh.c.hist[tid] = c;
+        }
+        __syncthreads();
+        select_bin(sh.c, sh.c.hist, krem);
+        const uint32_t bin = sh.c.bcast[0], ab = sh.c.bcast[1];
+        eq = sh.c.bcast[2];
+        __syncthreads();
+        abv += ab;
+        krem -= ab;
+        prefix |= bin << shift;
+        mask |= 255u << shift;
+    }
+    *above = abv;
+    *equal = eq;
+    return prefix;
+}
 
 __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t *__restrict__ ws_tok,
                                                                   const float *__restrict__ ws_score, int W_in,
@@ -840,31 +881,64 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
         return lo;
     };
 
-    // -- lower bound tau: the k-th largest of the first J entries of every beam
-    const int J = min(kk, (k_global + W_in - 1) / W_in + 1);
-    uint32_t a_, e_;
-    const uint32_t tau = radix_select<4>(sh.c, [&](auto fn) {
-        if (has_beam)
-            for (int j = 0; j < J; ++j) fn(key32(brow[j]));
-    }, k, &a_, &e_);
-    const int nb = has_beam ? prefix_ge(tau) : 0;
-
-    // -- exact cut among the prefixes
-    uint32_t above, n_eq;
-    const uint32_t kappa = radix_select<4>(sh.c, [&](auto fn) {
-        for (int j = 0; j < nb; ++j) fn(key32(brow[j]));
-    }, k, &above, &n_eq);
-    const uint32_t need = k - above;
-    // entries [0, gt_end) are above kappa, [gt_end, eq_end) equal it
-    const int gt_end = has_beam ? prefix_ge(kappa + 1u) : 0;   // finite scores: kappa < 0xffffffff
-    int eq_end = gt_end;
-    if (has_beam) {
-        int lo = gt_end, hi = nb;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (key32(brow[mid]) >= kappa) lo = mid + 1; else hi = mid;
+    uint32_t need;
+    int gt_end, eq_end;
+    // Fast path: the first C entries of every beam, all loaded at once. If every
+    // beam's later entries fall below the k-th largest of the loaded keys, the
+    // loaded keys hold the whole answer.
+    constexpr int C = 8;
+    const int cb = min(kk, C);
+    uint32_t kv[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) kv[j] = (has_beam && j < cb) ? key32(brow[j]) : 0u;   // 0: nothing (finite keys > 0)
+    bool fast = false;
+    if ((long long)W_in * cb >= (long long)k) {
+        uint32_t above0, eq0;
+        const uint32_t tau = radix_select32_w(sh, [&](auto fn) {
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                if (kv[j]) fn(kv[j]);
+        }, k, &above0, &eq0);
+        const bool complete = !has_beam || cb == kk || kv[cb - 1] < tau;   // later entries <= kv[cb-1]
+        if (__syncthreads_and(complete)) {
+            fast = true;
+            need = k - above0;
+            gt_end = 0;
+            eq_end = 0;
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                gt_end += kv[j] > tau;
+                eq_end += kv[j] >= tau;
+            }
         }
-        eq_end = lo;
+    }
+    if (!fast) {
+        // -- lower bound tau: the k-th largest of the first J entries of every beam
+        const int J = min(kk, (k_global + W_in - 1) / W_in + 1);
+        uint32_t a_, e_;
+        const uint32_t tau = radix_select<4>(sh.c, [&](auto fn) {
+            if (has_beam)
+                for (int j = 0; j < J; ++j) fn(key32(brow[j]));
+        }, k, &a_, &e_);
+        const int nb = has_beam ? prefix_ge(tau) : 0;
+
+        // -- exact cut among the prefixes
+        uint32_t above, n_eq;
+        const uint32_t kappa = radix_select<4>(sh.c, [&](auto fn) {
+            for (int j = 0; j < nb; ++j) fn(key32(brow[j]));
+        }, k, &above, &n_eq);
+        need = k - above;
+        // entries [0, gt_end) are above kappa, [gt_end, eq_end) equal it
+        gt_end = has_beam ? prefix_ge(kappa + 1u) : 0;   // finite scores: kappa < 0xffffffff
+        eq_end = gt_end;
+        if (has_beam) {
+            int lo = gt_end, hi = nb;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (key32(brow[mid]) >= kappa) lo = mid + 1; else hi = mid;
+            }
+            eq_end = lo;
+        }
     }
     uint32_t ties_total;
     const uint32_t tie_base = block_excl_scan(sh.c, (uint32_t)(eq_end - gt_end), &ties_total);
