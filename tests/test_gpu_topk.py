@@ -121,3 +121,49 @@ def test_determinism():
     r2 = bga().beam_topk(x, None, 100, 50, want_local=True, want_lse=True)
     for key in r1:
         assert torch.equal(r1[key], r2[key]), key
+
+
+def strided_sample_chunks(vocab, n_sample_chunks=512):
+    """The 8-logit chunks an evenly strided sample of a row visits (chunk i * n / s)."""
+    n = (vocab + 7) // 8
+    s = min(n, n_sample_chunks)
+    return np.unique((np.arange(s) * n) // s)
+
+
+def test_sample_that_misleads_the_threshold():
+    """Rows whose sampled chunks are all large: the sampled cut admits fewer
+    than k_local keys, so stage 1 must fall back to an exact select over the
+    whole row (and still match the oracle)."""
+    v = 20000
+    x = wl.make_logits(2, 3, v, 1.0, seed=21).float()
+    for c in strided_sample_chunks(v):
+        x[:, :, c * 8:(c + 1) * 8] += 6.0
+    x = x.to(torch.bfloat16)
+    run_and_check(x, None, 200, 6, "sample misleads")
+
+
+def test_candidates_spanning_many_keys():
+    """Logits spread over many binades: the keys at or above the cut span more
+    than the counting sort's bins, which takes the general path."""
+    g = torch.Generator().manual_seed(22)
+    mag = torch.exp2(torch.rand((2, 4, 10000), generator=g) * 123 - 120)   # |x| <= 8: the lse stays O(1)
+    sign = torch.where(torch.rand((2, 4, 10000), generator=g) < 0.5, -1.0, 1.0)
+    x = (mag * sign).to(torch.bfloat16)
+    run_and_check(x, None, 300, 8, "wide key range")
+
+
+def test_ties_beyond_the_candidate_list():
+    """Few distinct values in a long row: the keys at or above the cut exceed
+    the candidate list, and ties at the cut are resolved by lower id."""
+    g = torch.Generator().manual_seed(23)
+    x = torch.randint(-2, 3, (2, 3, 30000), generator=g).to(torch.bfloat16)
+    run_and_check(x, np.zeros((2, 3), np.float32), 64, 20, "ties beyond list")
+
+
+def test_one_beam_dominates_the_request():
+    """One beam's cumulative score dwarfs the others: all global winners come
+    from it, deeper than the first entries stage 2 loads up front."""
+    x = wl.make_logits(2, 50, 5000, 3.0, seed=24)
+    cum = np.zeros((2, 50), np.float32)
+    cum[:, 7] = 100.0
+    run_and_check(x, cum, 100, 50, "dominant beam")
