@@ -47,9 +47,10 @@ def lib():
                                                   f64, P, P, i32]
         L.oracle_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32]
         L.oracle_beam_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
+        L.oracle_beam_topk_given_lse.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
         L.oracle_num_threads.argtypes = [i32]
         for f in (L.oracle_packed_prefill, L.oracle_shared_prefix_decode, L.oracle_suffix_reorder,
-                  L.oracle_beam_topk, L.oracle_num_threads):
+                  L.oracle_beam_topk, L.oracle_beam_topk_given_lse, L.oracle_num_threads):
             f.restype = i32
         _lib = L
     return _lib
@@ -128,10 +129,11 @@ def suffix_reorder(src_k, src_v, parent, suffix_len, src_tokens=None, num_tokens
     return (dk, dv) if st is None else (dk, dv, dt)
 
 
-def beam_topk(logits, cum, k_local, k_global, nthreads: int = 0):
+def beam_topk(logits, cum, k_local, k_global, nthreads: int = 0, row_lse=None):
     """Two-stage selection. Returns a dict of numpy arrays:
     tokens/parents/scores [R,k_global], local_tokens/local_scores [R,W_in,k_local],
-    row_lse (fp32) and row_lse64 [R,W_in]."""
+    row_lse (fp32) and row_lse64 [R,W_in]. With `row_lse` ([R,W_in] fp32) given,
+    the rows' fp32 log-sum-exp is taken from it instead of computed."""
     x = _bits(logits)
     r, w_in, vocab = x.shape
     c = None if cum is None else np.ascontiguousarray(cum, dtype=np.float32)
@@ -141,9 +143,16 @@ def beam_topk(logits, cum, k_local, k_global, nthreads: int = 0):
         local_tokens=np.zeros((r, w_in, k_local), np.int32), local_scores=np.zeros((r, w_in, k_local), np.float32),
         row_lse=np.zeros((r, w_in), np.float32), row_lse64=np.zeros((r, w_in), np.float64),
     )
-    rc = lib().oracle_beam_topk(_p(x), _p(c), r, w_in, vocab, k_local, k_global, _p(out["tokens"]),
-                                _p(out["parents"]), _p(out["scores"]), _p(out["local_tokens"]),
-                                _p(out["local_scores"]), _p(out["row_lse"]), _p(out["row_lse64"]), nthreads)
+    if row_lse is None:
+        rc = lib().oracle_beam_topk(_p(x), _p(c), r, w_in, vocab, k_local, k_global, _p(out["tokens"]),
+                                    _p(out["parents"]), _p(out["scores"]), _p(out["local_tokens"]),
+                                    _p(out["local_scores"]), _p(out["row_lse"]), _p(out["row_lse64"]), nthreads)
+    else:
+        given = np.ascontiguousarray(row_lse, dtype=np.float32).reshape(r, w_in)
+        rc = lib().oracle_beam_topk_given_lse(_p(x), _p(c), _p(given), r, w_in, vocab, k_local, k_global,
+                                              _p(out["tokens"]), _p(out["parents"]), _p(out["scores"]),
+                                              _p(out["local_tokens"]), _p(out["local_scores"]), _p(out["row_lse"]),
+                                              _p(out["row_lse64"]), nthreads)
     if rc:
         raise ValueError(f"oracle_beam_topk rejected its arguments ({rc})")
     return out

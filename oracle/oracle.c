@@ -242,10 +242,28 @@ static double row_lse64(const uint16_t *x, int32_t V)
  *    parent = f / k_local, token = local id at (parent, f % k_local).
  * cum may be NULL (all zero). local_* / row_lse* outputs may be NULL.
  */
+/* Same selection with each row's fp32 log-sum-exp supplied by the caller
+ * (lse_in[R * W_in]) instead of computed: where floating point decides the
+ * integer result, this lets a test make that decision from the same fp32 row
+ * log-sum-exp on both sides. row_lse / row_lse_f64 then echo lse_in. */
+int32_t oracle_beam_topk_given_lse(const uint16_t *logits, const float *cum, const float *lse_in, int32_t R,
+                                   int32_t W_in, int32_t V, int32_t k_local, int32_t k_global, int32_t *out_tokens,
+                                   int32_t *out_parents, float *out_scores, int32_t *local_tokens,
+                                   float *local_scores, float *row_lse, double *row_lse_f64, int32_t nthreads);
+
 int32_t oracle_beam_topk(const uint16_t *logits, const float *cum, int32_t R, int32_t W_in, int32_t V,
                          int32_t k_local, int32_t k_global, int32_t *out_tokens, int32_t *out_parents,
                          float *out_scores, int32_t *local_tokens, float *local_scores, float *row_lse,
                          double *row_lse_f64, int32_t nthreads)
+{
+    return oracle_beam_topk_given_lse(logits, cum, NULL, R, W_in, V, k_local, k_global, out_tokens, out_parents,
+                                      out_scores, local_tokens, local_scores, row_lse, row_lse_f64, nthreads);
+}
+
+int32_t oracle_beam_topk_given_lse(const uint16_t *logits, const float *cum, const float *lse_in, int32_t R,
+                                   int32_t W_in, int32_t V, int32_t k_local, int32_t k_global, int32_t *out_tokens,
+                                   int32_t *out_parents, float *out_scores, int32_t *local_tokens,
+                                   float *local_scores, float *row_lse, double *row_lse_f64, int32_t nthreads)
 {
     if (!logits || !out_tokens || !out_parents || !out_scores) return 1;
     if (R < 0 || W_in <= 0 || V <= 0 || k_local <= 0 || k_local > V || k_global <= 0 ||
@@ -258,8 +276,8 @@ int32_t oracle_beam_topk(const uint16_t *logits, const float *cum, int32_t R, in
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (int64_t row = 0; row < rows; ++row) {
         const uint16_t *x = logits + row * V;
-        const double lse64 = row_lse64(x, V);
-        const float lse32 = (float)lse64;
+        const double lse64 = lse_in ? (double)lse_in[row] : row_lse64(x, V);
+        const float lse32 = lse_in ? lse_in[row] : (float)lse64;
         by_logit *e = malloc(sizeof(by_logit) * V);
         for (int32_t v = 0; v < V; ++v) { e[v].x = widen_f(x[v]); e[v].id = v; }
         qsort(e, (size_t)V, sizeof *e, cmp_logit);

@@ -2,10 +2,12 @@
 
 Stage-1 token ids depend only on the bf16 logits and must match bit for bit.
 Scores depend on each row's fp32 log-sum-exp; the GPU's must be within 1e-5 of
-the oracle's (fp64, rounded to fp32). Final ids, parents and scores must then
-match bit for bit; a request may differ only where a row's GPU log-sum-exp
-differs from the oracle's fp32 value, and then the GPU result must still be
-exactly the (-score, flat index) top-k of the GPU's own stage-1 scores.
+the oracle's (fp64, rounded to fp32). Where that floating-point value decides
+the integer results, both sides decide from the same value: the oracle run
+with the GPU's row log-sum-exp must match every output bit for bit. Against
+the oracle's own log-sum-exp, a request may differ only where a row's GPU value
+differs from the oracle's fp32 value, and the GPU result must still be exactly
+the (-score, flat index) top-k of the GPU's own stage-1 scores.
 """
 import numpy as np
 import pytest
@@ -53,6 +55,11 @@ def run_and_check(x, cum, k_local, k_global, name):
     c = np.zeros(x.shape[:2], np.float32) if cum is None else cum
     lp = np.take_along_axis(xs, lt, axis=2) - glse[:, :, None]
     assert np.array_equal(res["local_scores"].cpu().numpy(), c[:, :, None] + lp), "stage-1 scores"
+    # where floating point decides the selection, both sides decide from the same
+    # fp32 row log-sum-exp (the kernel's): then everything must match bit for bit
+    same_lse = oracle.beam_topk(x.cpu(), cum, k_local, k_global, row_lse=glse)
+    for key in ("local_tokens", "local_scores", "tokens", "parents", "scores"):
+        assert np.array_equal(res[key].cpu().numpy(), same_lse[key]), f"{key} differ given the same row lse"
     n_mismatch = 0
     for i in range(x.shape[0]):
         same = (np.array_equal(res["tokens"][i].cpu().numpy(), ref["tokens"][i])

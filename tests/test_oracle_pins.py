@@ -360,3 +360,21 @@ def test_state_size_shared_prefix_vs_per_beam():
     assert wl.state_elems_shared_prefix(480, 400, 5, 8, 128) == (480 + 400 * 5) * 8 * 128
     assert wl.state_elems_per_beam(480, 400, 5, 8, 128) == 400 * (480 + 5) * 8 * 128
     assert wl.decode_bytes(32, 100, 16, 8, 128, 1, 64) == 28_254_208
+
+
+def test_beam_topk_given_lse_reproduces_own_lse():
+    """Supplying the oracle's own fp32 row log-sum-exp reproduces its outputs
+    bit for bit; a shifted log-sum-exp shifts every stage-1 score by one fp32
+    subtraction and leaves the stage-1 ids unchanged."""
+    x = wl.make_logits(2, 4, 700, 2.0, seed=31)
+    cum = np.array([[0, -1, -2, -3], [-0.5, -0.25, 0, -4]], np.float32)
+    a = oracle.beam_topk(x, cum, 12, 6)
+    b = oracle.beam_topk(x, cum, 12, 6, row_lse=a["row_lse"])
+    for key in ("local_tokens", "local_scores", "tokens", "parents", "scores"):
+        assert np.array_equal(a[key], b[key]), key
+    shifted = (a["row_lse"] + np.float32(0.5)).astype(np.float32)
+    c = oracle.beam_topk(x, cum, 12, 6, row_lse=shifted)
+    assert np.array_equal(c["local_tokens"], a["local_tokens"])
+    xs = x.float().numpy()
+    lp = np.take_along_axis(xs, c["local_tokens"], axis=2) - shifted[:, :, None]
+    assert np.array_equal(c["local_scores"], cum[:, :, None] + lp)
