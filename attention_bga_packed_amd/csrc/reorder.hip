@@ -29,11 +29,28 @@ __global__ __launch_bounds__(256) void suffix_reorder_kernel(
     u32x4 *dk = (u32x4 *)(dst_k + dst_off);
     u32x4 *dv = (u32x4 *)(dst_v + dst_off);
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < run16; i += blockDim.x) {
-        const u32x4 a = ok ? sk[i] : zero;
-        const u32x4 b = ok ? svv[i] : zero;
-        dk[i] = a;
-        dv[i] = b;
+    // up to 4 chunks of K and of V per thread in flight before any store
+    constexpr int U = 4;
+    for (int i0 = 0; i0 < run16; i0 += U * 256) {
+        u32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * 256 + (int)threadIdx.x;
+            a[u] = zero;
+            b[u] = zero;
+            if (ok && i < run16) {
+                a[u] = sk[i];
+                b[u] = svv[i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * 256 + (int)threadIdx.x;
+            if (i < run16) {
+                dk[i] = a[u];
+                dv[i] = b[u];
+            }
+        }
     }
     if (src_tok) {
         const int32_t *st = src_tok + ((size_t)r * W + (ok ? p : 0)) * tok_cap;
