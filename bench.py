@@ -12,8 +12,10 @@ One step = one pass of the whole hot path over synthetic inputs:
 
 The headline value is the prefill attention throughput in logical TFLOP/s
 (4 * D * Nq * sum L(L+1)/2 per layer, FMA = 2); decode, top-K and reorder are
-reported in algorithmic GB/s. Kernel times come from HIP events around every
-launch on the launching stream. Inputs are drawn on the GPU from fixed seeds.
+reported in algorithmic GB/s. Kernel times come from HIP events on the launching
+stream: one pair around the 28 back-to-back prefill launches of a request (the
+average launch is their span / 28) and one pair around every beam-search launch.
+Inputs are drawn on the GPU from fixed seeds.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -138,15 +140,16 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
 
     def step(timed):
-        """One pass of the hot path; with `timed`, HIP events bracket every launch."""
-        i = 0
+        """One pass of the hot path; with `timed`, HIP events bracket the prefill layers and every
+        beam-search launch."""
+        # the 28 layers run back to back, as in a request; one event pair spans them
+        if timed:
+            evs[0][0].record(stream)
         for c in cases:
-            if timed:
-                evs[i][0].record(stream)
             bga.packed_gqa_prefill(c.q, c.k, c.v, cu, max_len, out=p_out, lse=p_lse)
-            if timed:
-                evs[i][1].record(stream)
-            i += 1
+        if timed:
+            evs[0][1].record(stream)
+        i = layers
         cur = 0
         cum.zero_()
         for s in range(NS):
@@ -179,10 +182,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # ---- per-kernel durations: the same K steps again, HIP events around every launch on the
-    # launching stream. A spin kernel queued first holds the GPU while the host enqueues the whole
-    # step, so the launches run back to back and each event pair spans only its kernel (otherwise
-    # the host's per-launch overhead, which exceeds a prefill launch, would be counted too).
+    # ---- per-kernel durations: the same K steps again, HIP events on the launching stream. A spin
+    # kernel queued first holds the GPU while the host enqueues the whole step, so the launches run
+    # back to back and the event pairs span only the kernels (otherwise the host's per-launch
+    # overhead, which exceeds a prefill launch, would be counted too).
     host_t = time.perf_counter()
     step(True)
     host_t = time.perf_counter() - host_t
@@ -195,7 +198,7 @@ def main():
     cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
     gate = int(cycles_per_ms * max(3.0 * host_t * 1e3, 2.0))
 
-    t_pre = [0.0] * layers
+    t_pre = 0.0
     t_dec = [0.0] * NS
     t_top = [0.0] * NS
     t_reo = [0.0] * NS
@@ -203,8 +206,7 @@ def main():
         torch.cuda._sleep(gate)
         step(True)
         torch.cuda.synchronize()   # events of this step are complete; read them
-        for l in range(layers):
-            t_pre[l] += evs[l][0].elapsed_time(evs[l][1])
+        t_pre += evs[0][0].elapsed_time(evs[0][1])
         for s in range(NS):
             j = layers + 3 * s
             t_dec[s] += evs[j][0].elapsed_time(evs[j][1])
@@ -213,7 +215,7 @@ def main():
 
     K = args.steps
     pre_flops = wl.prefill_flops(lengths, pcfg["nq"], pcfg["d"])
-    pre_ms = sum(t_pre) / (K * layers)                      # average launch, ms
+    pre_ms = t_pre / (K * layers)                           # average launch, ms
     pre_tflops = pre_flops / (pre_ms * 1e-3) / 1e12
     dec_bytes = [wl.decode_bytes(R, W, NQ, NKV, LP, s + 1, D) for s in range(NS)]
     dec_ms = [t / K for t in t_dec]
