@@ -7,105 +7,166 @@
 // valid K/V range from the boundary and scans it blockwise with an fp32 online
 // softmax.
 //
-// Work unit = (kv head g, sequence, query tile of BM = 32*TS tokens). The
-// workgroup holds H*TS waves (H = up to 8 of the group's G query heads at
-// d 128, up to 4 at d 64; larger groups are split over several workgroups):
-// wave w serves one query head for the 32 tokens of sub-tile w / H, so every
-// K/V tile staged in LDS is shared by H query heads and TS sub-tiles. Keys run
-// from the start of the sequence to the end of the query tile; only tiles
-// that reach past a wave's first query are masked.
+// Rows. For a (sequence, kv head g) the query rows are the pairs (token t,
+// head h of the group), n = t * G + h, t < L. A workgroup of NW waves takes
+// 32 * NW consecutive rows; every wave takes 32 of them. All G heads of a token
+// sit in the same block, so one K/V tile staged in LDS serves the whole group,
+// and a block is full whatever G is (no idle head slots).
 //
-// Grid = (Nkv * splits, B, max tiles per sequence). The tile index is reversed so the
-// longest (last) query tiles of every sequence are dispatched first. With
-// consecutive workgroups dealt round-robin over the 8 XCDs, putting the kv head
-// in x keeps all tiles of one (sequence, kv head) on the same XCD (and L2)
-// when Nkv is a multiple of 8.
-#include "attn_tile.hpp"
+// Keys. The workgroup scans the sequence's keys from its first token up to its
+// last row's token, 64 at a time. A wave computes only the tiles up to its own
+// last row's token (it still takes part in the copies and barriers of the
+// later ones) and masks only the tiles that reach past its first row's token.
+//
+// Grid = (pairs rounded up to a multiple of 8, row blocks). Pair = (sequence,
+// kv head). The row-block index is reversed, so the longest (last) blocks of
+// every sequence are dispatched first. Consecutive workgroups are dealt
+// round-robin over the 8 XCDs, so the pair index in x, padded to a multiple of
+// 8, keeps every block of one (sequence, kv head) on one XCD and its L2.
+#include <type_traits>
+
+#include "attn_core.hpp"
 #include "internal.hpp"
 
 namespace bga {
 
-// NW: waves per workgroup when fixed at compile time (0: any)
+using namespace core;
+
 template <int D, int NW>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void packed_prefill_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void packed_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ cu, int nq, int nkv, int group, int hsplit, int hpw, int ts_per_wg, float scale,
+    const int32_t *__restrict__ cu, int num_pairs, int nq, int nkv, int group, float scale,
     uint16_t *__restrict__ out, float *__restrict__ lse)
 {
-    using T = AttnTile<D>;
+    using G = Geo<D>;
+    constexpr int ROWS = 32 * NW;
     extern __shared__ __align__(16) uint16_t smem[];
 
-    const int g = blockIdx.x / hsplit, split = blockIdx.x % hsplit, seq = blockIdx.y;
-    const int bm = 32 * ts_per_wg;
-    const int tile = gridDim.z - 1 - blockIdx.z;
-    const int s0 = cu[seq], s1 = cu[seq + 1];
-    const int q_lo = s0 + tile * bm;
-    if (q_lo >= s1) return;  // uniform over the workgroup
-    const int kend = min(q_lo + bm, s1);
-    const int nkt = (kend - s0 + T::BN - 1) / T::BN;
+    const int pair = blockIdx.x;
+    if (pair >= num_pairs) return;
+    const int seq = __builtin_amdgcn_readfirstlane(pair / nkv), g = pair - seq * nkv;
+    const int s0 = cu[seq];
+    const int nrows = (cu[seq + 1] - s0) * group;
+    const int n0 = (gridDim.y - 1 - blockIdx.y) * ROWS;
+    if (n0 >= nrows) return;   // uniform over the workgroup
 
-    const int nthr = blockDim.x;
-    const int w = threadIdx.x >> 6, col = threadIdx.x & 31;
-    const int hig = split * hpw + (w % hpw);   // head within the group
-    const int head = g * group + min(hig, group - 1);
-    const int qw0 = q_lo + (w / hpw) * 32;
-    const int qtok = qw0 + col;
-    const bool wave_active = qw0 < s1 && hig < group;
-    const bool row_valid = qtok < s1 && wave_active;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63, col = lane & 31;
+
+    // Wave-uniform values: integer division runs on the vector ALU, so the
+    // quotients are read back from the first lane to keep the control flow scalar.
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    // keys [0, kend) of the sequence; tiles [0, nkt)
+    const int kend = uni((min(n0 + ROWS, nrows) - 1) / group + 1);
+    const int nkt = uni((kend + G::BN - 1) / G::BN);
+    // this wave: rows [wr0, wr_last], tiles [0, nkt_w), masked from tile kt_mask on
+    const int wr0 = n0 + wave * 32;
+    const int wr_last = min(wr0 + 31, nrows - 1);
+    const int nkt_w = uni(wr0 < nrows ? (wr_last / group) / G::BN + 1 : 0);
+    const int kt_mask = uni((wr0 / group + 1) / G::BN);
+
+    // this lane's row (rows past the end duplicate the last row; not stored)
+    const int n = min(wr0 + col, nrows - 1);
+    const int tok = n / group, h = n - tok * group;
+    const size_t qrow = ((size_t)(s0 + tok) * nq + (size_t)g * group + h);
 
     bf16x8 qop[D / 16];
-    load_q_operand<D>(qop, q + ((size_t)qtok * nq + head) * D, row_valid);
+    const uint32_t lds_base = (uint32_t)(size_t)(const BGA_LDS char *)smem;
+    const uint32_t rbytes = (uint32_t)(nkv * D * 2);
+    const uint64_t kbase = uni64((uint64_t)(size_t)(k + ((size_t)s0 * nkv + g) * D));
+    const uint64_t vbase = uni64((uint64_t)(size_t)(v + ((size_t)s0 * nkv + g) * D));
+    const uint64_t tile_bytes = (uint64_t)G::BN * rbytes;
+    auto last_row = [&](int kt) { return kt * G::BN + G::BN > kend ? kend - 1 - kt * G::BN : -1; };
 
-    const BGA_LDS char *lds = lds_ptr(smem);
-    const uint32_t lds_base = lds_addr(lds);
-    WaveAttn<D> st;
-    st.init(lds);
+    Copier<D, NW> cp;
+    cp.init(wave, rbytes);
+    cp.template issue<false>(lds_base + G::kslot(0), kbase, last_row(0));
+    cp.template issue<true>(lds_base + G::vslot(0), vbase, last_row(0));
+    load_q<D>(qop, q + qrow * D);
+
+    Reads<D> rd;
+    rd.init(lds_base);
+    Wave<D> st;
+    st.reset();
     const float c2 = scale * kLog2e;
-    const uint32_t row_stride = (uint32_t)(nkv * D);
-    DmaPlan<D, NW> plan;
-    plan.init(w, nthr >> 6);
-    // tile kt needs masking when it reaches past this wave's first query; tiles
-    // entirely after the wave's last query are fully masked (contribute zero)
-    auto need_mask = [&](int kt) { return s0 + kt * AttnTile<D>::BN + AttnTile<D>::BN - 1 > qw0; };
-    attn_scan<D>(st, plan, lds_base, qop, k + (size_t)g * D, v + (size_t)g * D, row_stride, s0, kend, nkt, c2,
-                 need_mask, qtok);
-    if (!wave_active) return;
-    st.finish(out + ((size_t)qtok * nq + head) * D, lse ? lse + (size_t)qtok * nq + head : nullptr, row_valid,
-              scale);
+
+    wait_copies_and_sync();
+    if (nkt > 1) cp.template issue<false>(lds_base + G::kslot(1), kbase + tile_bytes, last_row(1));
+
+    f32x16 sa[2], sb[2];
+    if (nkt_w > 0) {
+        Wave<D>::scores(rd, qop, G::kslot(0), sa);
+        if (kt_mask == 0) Wave<D>::mask(sa, tok);
+        st.m = Wave<D>::rowmax(sa);
+        st.mc = st.m * c2;
+    }
+
+    // Tile kt: K(kt) and V(kt) sit in slot kt & 1. Every tile starts with a
+    // barrier after which K(kt+2) and V(kt+1) are copied into the slots that
+    // K(kt) and V(kt-1) held.
+    auto sync_and_copy = [&](int kt) {
+        wait_copies_and_sync();   // K(kt+1), V(kt) landed; K(kt), V(kt-1) no longer read
+        const uint32_t p = (uint32_t)(kt & 1);
+        if (kt + 2 < nkt)
+            cp.template issue<false>(lds_base + p * G::KBYTES, kbase + (uint64_t)(kt + 2) * tile_bytes,
+                                     last_row(kt + 2));
+        if (kt + 1 < nkt)
+            cp.template issue<true>(lds_base + G::vslot(0) + (1 - p) * G::KBYTES,
+                                    vbase + (uint64_t)(kt + 1) * tile_bytes, last_row(kt + 1));
+    };
+    // all but the wave's last tile: exponentials and P*V of tile kt, scores of kt+1
+    auto step = [&](int kt, auto parity, f32x16(&sc)[2], f32x16(&sn)[2]) {
+        constexpr int P = decltype(parity)::value;
+        sync_and_copy(kt);
+        float mx = st.step(rd, qop, sc, sn, G::kslot(1 - P), G::vslot(P), c2);
+        if (kt + 1 >= kt_mask) {   // the next tile reaches past this wave's first row
+            Wave<D>::mask(sn, tok - (kt + 1) * G::BN);
+            mx = Wave<D>::rowmax(sn);
+        }
+        st.update_max(mx, c2);
+    };
+    const int klast = nkt_w - 1;
+    int kt = 0;
+    for (; kt + 1 < klast; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{}, sa, sb);
+        step(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
+    }
+    if (kt < klast) {
+        step(kt, std::integral_constant<int, 0>{}, sa, sb);
+        ++kt;
+    }
+    // the wave's last tile
+    if (kt == klast) {
+        sync_and_copy(kt);
+        if ((kt & 1) == 0)
+            st.last(rd, sa, G::vslot(0), c2);
+        else
+            st.last(rd, sb, G::vslot(1), c2);
+        ++kt;
+    }
+    // the workgroup's remaining tiles: copies and barriers only
+    for (; kt < nkt; ++kt) sync_and_copy(kt);
+
+    if (nkt_w == 0) return;
+    st.finish(out + qrow * D, lse ? lse + qrow : nullptr, wr0 + col < nrows, scale);
 }
 
-template <int D>
+template <int D, int NW>
 static hipError_t launch_prefill_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu,
                                    int num_seqs, int max_seqlen, int nq, int nkv, float scale, uint16_t *out,
                                    float *lse, hipStream_t stream)
 {
     const int group = nq / nkv;
-    // At d 64 a wave fits in 168 registers (3 waves per SIMD, 12 per CU): groups are
-    // split into workgroups of <= 4 query heads so that several workgroups share a
-    // CU and one's prologue and epilogue overlap another's tiles. At d 128 (2 waves
-    // per SIMD) up to 8 heads share a workgroup.
-    const int hsplit = D == 64 ? (group + 3) / 4 : (group + 7) / 8;
-    const int hpw = (group + hsplit - 1) / hsplit;
-    const int ts = hpw >= 4 ? 1 : (hpw == 1 ? 4 : 2); // >= 4 waves per workgroup
-    const int bm = 32 * ts;
-    const int tiles = (max_seqlen + bm - 1) / bm;
-    const int nw = hpw * ts;
-    const void *kern = nw == 4   ? (const void *)packed_prefill_kernel<D, 4>
-                       : nw == 8 ? (const void *)packed_prefill_kernel<D, 8>
-                                 : (const void *)packed_prefill_kernel<D, 0>;
-    const size_t smem = AttnTile<D>::SMEM_BYTES;
+    const int pairs = num_seqs * nkv;
+    const int xdim = (pairs + 7) / 8 * 8;
+    const int blocks = (int)(((int64_t)max_seqlen * group + 32 * NW - 1) / (32 * NW));
+    const size_t smem = Geo<D>::SMEM;
+    const void *kern = (const void *)packed_prefill_kernel<D, NW>;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    dim3 grid(nkv * hsplit, num_seqs, tiles), block(64 * nw);
-    if (nw == 4)
-        hipLaunchKernelGGL((packed_prefill_kernel<D, 4>), grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit,
-                           hpw, ts, scale, out, lse);
-    else if (nw == 8)
-        hipLaunchKernelGGL((packed_prefill_kernel<D, 8>), grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit,
-                           hpw, ts, scale, out, lse);
-    else
-        hipLaunchKernelGGL((packed_prefill_kernel<D, 0>), grid, block, smem, stream, q, k, v, cu, nq, nkv, group, hsplit,
-                           hpw, ts, scale, out, lse);
+    dim3 grid(xdim, blocks), block(64 * NW);
+    hipLaunchKernelGGL((packed_prefill_kernel<D, NW>), grid, block, smem, stream, q, k, v, cu, pairs, nq, nkv, group,
+                       scale, out, lse);
     return hipGetLastError();
 }
 
@@ -113,8 +174,8 @@ hipError_t launch_packed_prefill(const uint16_t *q, const uint16_t *k, const uin
                                  int num_seqs, int max_seqlen, int nq, int nkv, int d, float scale, uint16_t *out,
                                  float *lse, hipStream_t stream)
 {
-    if (d == 64) return launch_prefill_d<64>(q, k, v, cu, num_seqs, max_seqlen, nq, nkv, scale, out, lse, stream);
-    return launch_prefill_d<128>(q, k, v, cu, num_seqs, max_seqlen, nq, nkv, scale, out, lse, stream);
+    if (d == 64) return launch_prefill_d<64, 4>(q, k, v, cu, num_seqs, max_seqlen, nq, nkv, scale, out, lse, stream);
+    return launch_prefill_d<128, 4>(q, k, v, cu, num_seqs, max_seqlen, nq, nkv, scale, out, lse, stream);
 }
 
 }  // namespace bga
