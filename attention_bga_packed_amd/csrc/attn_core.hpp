@@ -39,6 +39,8 @@
 // (numerator and denominator use the same reference).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 #define BGA_LDS __attribute__((address_space(3)))
@@ -119,7 +121,7 @@ struct Copier {
 
     __device__ __forceinline__ void init(int wave_, uint32_t rbytes_)
     {
-        const int lane = threadIdx.x & 63;
+        const int lane = lane_id();
         wave = wave_;
         rbytes = rbytes_;
         lrow = lane / G::CHUNKS;
@@ -170,7 +172,7 @@ struct Reads {
 
     __device__ __forceinline__ void init(uint32_t lds_base)
     {
-        const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+        const int lane = lane_id(), col = lane & 31, half = lane >> 5;
         // rows col and col + 32 share the K swizzle (period 16)
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
@@ -219,6 +221,13 @@ template <int D>
 struct Wave {
     using G = Geo<D>;
     static constexpr float kLazy = 8.f;   // log2 of the largest unnormalised probability kept
+    static constexpr int KLA = D == 128 ? 2 : 2;   // K operand reads issued this many MFMAs ahead
+    static constexpr int VLA = D == 128 ? 2 : 2;   // V^T operand reads issued this many MFMAs ahead
+    // exponential pairs computed beside the score MFMAs (the rest ride on the
+    // first half of the P*V MFMAs; all of the first 32 keys' pairs, 0..7, must
+    // be among the former)
+    static constexpr int E1 = D == 128 ? 12 : 12;
+    static_assert(E1 >= 8 && E1 <= 16, "pairs of keys 0..31 feed the first P*V MFMAs");
 
     f32x16 o[D / 32];   // O^T: lane holds row (lane & 31), d = b*32 + (r/4)*8 + (lane>>5)*4 + r%4
     float m;            // reference maximum of the raw scores q.k (unscaled)
@@ -227,6 +236,7 @@ struct Wave {
     uint32_t pk[2][8];  // bf16 P^T of the current tile: pk[kb][j] = keys of elements 2j, 2j+1
     float psum;
 
+    // empty state: no keys seen
     __device__ __forceinline__ void reset()
     {
 #pragma unroll
@@ -234,6 +244,8 @@ struct Wave {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
         l = 0.f;
+        m = -INFINITY;
+        mc = -INFINITY;
     }
 
     // probabilities of value pair p (0..15) of tile scores s: block p / 8, elements 2(p%8), 2(p%8)+1
@@ -259,7 +271,7 @@ struct Wave {
     // first key has offset 0).
     __device__ __forceinline__ static void mask(f32x16 (&s)[2], int lim_tile)
     {
-        const int half = (threadIdx.x & 63) >> 5;
+        const int half = lane_id() >> 5;
         const int lim = lim_tile - half * 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -324,42 +336,41 @@ struct Wave {
     {
         constexpr int NS = G::NS;
         const f32x16 z = {};
-        // phase 1: NS score MFMAs (operands two ahead) with exponential pairs 0..11
-        u32x4 ka[3];
-        ka[0] = rd.kop(0, kn_off);
-        ka[1] = rd.kop(0, kn_off + 32 * G::ROWB);
+        // phase 1: NS score MFMAs (operands KLA ahead) with exponential pairs 0..E1-1
+        auto kread = [&](int j) { return rd.kop(j >> 1, kn_off + (uint32_t)((j & 1) * 32 * G::ROWB)); };
+        u32x4 ka[KLA + 1];
+#pragma unroll
+        for (int j = 0; j < KLA; ++j) ka[j] = kread(j);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            if (i + 2 < NS) {
-                const int j = i + 2;
-                ka[j % 3] = rd.kop(j >> 1, kn_off + (uint32_t)((j & 1) * 32 * G::ROWB));
-            }
+            if (i + KLA < NS) ka[(i + KLA) % (KLA + 1)] = kread(i + KLA);
             const int ks = i >> 1, kb = i & 1;
-            sn[kb] = mfma32x32x16(as_bf16x8(ka[i % 3]), qop[ks], ks == 0 ? z : sn[kb]);
+            sn[kb] = mfma32x32x16(as_bf16x8(ka[i % (KLA + 1)]), qop[ks], ks == 0 ? z : sn[kb]);
 #pragma unroll
-            for (int p = i * 12 / NS; p < (i + 1) * 12 / NS; ++p) exp_pair(sc, p, c2);
+            for (int p = i * E1 / NS; p < (i + 1) * E1 / NS; ++p) exp_pair(sc, p, c2);
             fence();
         }
         // phase 2: the 4 * NB P*V MFMAs in order (key block kb, 16-key half kk,
-        // d block b), operands two ahead; exponential pairs 12..15 ride on the
+        // d block b), operands VLA ahead; exponential pairs E1..15 ride on the
         // first half (keys 0..31), the next tile's row maximum on the second
         constexpr int NPV = 4 * G::NB;
         auto vread = [&](int mi) {
             const int kb = mi / (2 * G::NB), kk = (mi / G::NB) & 1, b = mi % G::NB;
             return rd.vop(b, vs_off + (uint32_t)((kb * 32 + kk * 16) * G::ROWB));
         };
-        u32x4 va[3];
-        va[0] = vread(0);
-        va[1] = vread(1);
+        u32x4 va[VLA + 1];
+#pragma unroll
+        for (int j = 0; j < VLA; ++j) va[j] = vread(j);
         float mx = 0.f;
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
-            if (i + 2 < NPV) va[(i + 2) % 3] = vread(i + 2);
+            if (i + VLA < NPV) va[(i + VLA) % (VLA + 1)] = vread(i + VLA);
             const int kb = i / (2 * G::NB), kk = (i / G::NB) & 1, b = i % G::NB;
-            pv(kb, kk, b, va[i % 3]);
+            pv(kb, kk, b, va[i % (VLA + 1)]);
             if (i < NPV / 2) {
 #pragma unroll
-                for (int p = 12 + i * 8 / NPV; p < 12 + (i + 1) * 8 / NPV; ++p) exp_pair(sc, p, c2);
+                for (int p = E1 + i * 2 * (16 - E1) / NPV; p < E1 + (i + 1) * 2 * (16 - E1) / NPV; ++p)
+                    exp_pair(sc, p, c2);
                 if (i == NPV / 2 - 1) l += psum;
             } else if (i == NPV / 2) {
                 mx = rowmax(sn);
@@ -397,11 +408,12 @@ struct Wave {
         l += psum;
     }
 
-    // Normalise and store this lane's row: orow = its output row [D], lse_ptr its
-    // fp32 slot (or nullptr). Lanes l and l ^ 32 hold the two halves of the row.
+    // Final normalisation and stores for this lane's row: orow = its output row
+    // [D], lse_ptr its fp32 slot (or nullptr). Lanes l and l ^ 32 hold the two
+    // halves of the row.
     __device__ __forceinline__ void finish(uint16_t *orow, float *lse_ptr, bool store, float scale)
     {
-        const int lane = threadIdx.x & 63, half = lane >> 5;
+        const int lane = lane_id(), half = lane >> 5;
         const float lt = pair_sum(l);
         const float inv = 1.f / lt;
         if (!store) return;
@@ -418,12 +430,92 @@ struct Wave {
     }
 };
 
+// The blocked scan over keys [0, kend) of one K/V range, shared by the
+// prefill and decode kernels. Tile kt holds keys 64 kt + [0, 64); K/V row `key`
+// lives at byte address kbase / vbase + key * row stride. Every wave of the
+// workgroup calls this (it holds the barriers) with the workgroup's tile count
+// nkt; the wave computes tiles [0, nkt_w) only. Keys past `lim` (this lane's
+// last allowed key) are masked in tiles kt >= kt_mask. The caller has issued
+// the copies of tile 0 (K0, V0) and waited for them (wait_copies_and_sync);
+// the state st is empty when `fresh`, else it may already hold keys. When
+// `resident`, nkt <= 2 and tiles [0, nkt) already sit in their slots (a previous
+// scan of the same keys left them there): nothing is copied.
+template <int D, int NW>
+__device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copier<D, NW> &cp, const bf16x8 *qop,
+                                     uint32_t lds_base, uint64_t kbase, uint64_t vbase, int kend, int nkt, int nkt_w,
+                                     int lim, int kt_mask, float c2, bool fresh, bool resident = false)
+{
+    using G = Geo<D>;
+    const uint64_t tile_bytes = (uint64_t)G::BN * cp.rbytes;
+    auto last_row = [&](int kt) { return kt * G::BN + G::BN > kend ? kend - 1 - kt * G::BN : -1; };
+    if (nkt > 1 && !resident) cp.template issue<false>(lds_base + G::kslot(1), kbase + tile_bytes, last_row(1));
+
+    f32x16 sa[2], sb[2];
+    if (nkt_w > 0) {
+        Wave<D>::scores(rd, qop, G::kslot(0), sa);
+        if (kt_mask == 0) Wave<D>::mask(sa, lim);
+        const float mx = Wave<D>::rowmax(sa);
+        if (fresh) {   // every row has a key in tile 0
+            st.m = mx;
+            st.mc = mx * c2;
+        } else {
+            st.update_max(mx, c2);
+        }
+    }
+    // Tile kt: K(kt) and V(kt) sit in slot kt & 1. Every tile starts with a
+    // barrier after which K(kt+2) and V(kt+1) are copied into the slots that
+    // K(kt) and V(kt-1) held.
+    auto sync_and_copy = [&](int kt) {
+        wait_copies_and_sync();   // K(kt+1), V(kt) landed; K(kt), V(kt-1) no longer read
+        if (resident) return;
+        const uint32_t p = (uint32_t)(kt & 1);
+        if (kt + 2 < nkt)
+            cp.template issue<false>(lds_base + p * G::KBYTES, kbase + (uint64_t)(kt + 2) * tile_bytes,
+                                     last_row(kt + 2));
+        if (kt + 1 < nkt)
+            cp.template issue<true>(lds_base + G::vslot(0) + (1 - p) * G::KBYTES,
+                                    vbase + (uint64_t)(kt + 1) * tile_bytes, last_row(kt + 1));
+    };
+    // all but the wave's last tile: exponentials and P*V of tile kt, scores of kt+1
+    auto step = [&](int kt, auto parity, f32x16(&sc)[2], f32x16(&sn)[2]) {
+        constexpr int P = decltype(parity)::value;
+        sync_and_copy(kt);
+        float mx = st.step(rd, qop, sc, sn, G::kslot(1 - P), G::vslot(P), c2);
+        if (kt + 1 >= kt_mask) {   // the next tile has keys past some row's limit
+            Wave<D>::mask(sn, lim - (kt + 1) * G::BN);
+            mx = Wave<D>::rowmax(sn);
+        }
+        st.update_max(mx, c2);
+    };
+    const int klast = nkt_w - 1;
+    int kt = 0;
+    for (; kt + 1 < klast; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{}, sa, sb);
+        step(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
+    }
+    if (kt < klast) {
+        step(kt, std::integral_constant<int, 0>{}, sa, sb);
+        ++kt;
+    }
+    // the wave's last tile
+    if (kt == klast) {
+        sync_and_copy(kt);
+        if ((kt & 1) == 0)
+            st.last(rd, sa, G::vslot(0), c2);
+        else
+            st.last(rd, sb, G::vslot(1), c2);
+        ++kt;
+    }
+    // the workgroup's remaining tiles: copies and barriers only
+    for (; kt < nkt; ++kt) sync_and_copy(kt);
+}
+
 // Q^T operand of one lane: query row `qrow` (D elements), k slots (lane>>5)*8 + [0,8)
 // of every 16-wide d step.
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 *qop, const uint16_t *qrow)
 {
-    const int half = (threadIdx.x & 63) >> 5;
+    const int half = lane_id() >> 5;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qop[ks] = as_bf16x8(*(const u32x4 *)(qrow + ks * 16 + half * 8));
 }

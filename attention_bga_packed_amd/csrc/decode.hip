@@ -7,22 +7,26 @@
 // without any concatenated tensor.
 //
 // The prefix segment is the dense part: for a (request, kv head) all W beams'
-// G query heads form a [W*G, D] block that multiplies the same [L_p, D] prefix,
-// so it runs on MFMA exactly like a prefill tile (no mask except the ragged end
-// of the prefix). A workgroup takes 128 of those query rows (4 waves x 32) and
-// streams the prefix through LDS once; the prefix is therefore read from HBM
-// once per (request, kv head) and from L2 by the other row blocks. The suffix
-// segment is a handful of per-beam keys: each lane pair (lanes l and l^32, one
-// query row) forms the dot products with its own beam's suffix keys from the
-// d-halves it already holds and folds them into the same (m, l, O) state.
+// G query heads form a [W*G, D] block (rows n = beam * G + head) that multiplies
+// the same [L_p, D] prefix, so it runs on MFMA exactly like a prefill tile, with
+// no mask except the ragged end of the prefix. A workgroup takes 128 of those
+// query rows (4 waves x 32) and streams the prefix through LDS once; the prefix
+// is therefore read from HBM once per (request, kv head) and from L2 by the
+// other row blocks. The suffix segment is a handful of per-beam keys: each lane
+// pair (lanes l and l^32, one query row) forms the dot products with its own
+// beam's suffix keys from the d-halves it already holds and folds them into the
+// same (m, l, O) state. Every row takes the same order (prefix, then suffix), so
+// a row's result does not depend on which workgroup holds it.
 //
 // Grid = (R*Nkv, row blocks). Consecutive workgroups are dealt round-robin over
 // the 8 XCDs, so with R*Nkv a multiple of 8 every row block of one
 // (request, kv head) lands on the same XCD and shares its L2 copy of the prefix.
-#include "attn_tile.hpp"
+#include "attn_core.hpp"
 #include "internal.hpp"
 
 namespace bga {
+
+using namespace core;
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void shared_prefix_decode_kernel(
@@ -30,106 +34,94 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const uint16_t *__restrict__ sk, const uint16_t *__restrict__ sv, int W, int Lp, int Ls, int Ls_cap, int nq,
     int nkv, int group, float scale, uint16_t *__restrict__ out, float *__restrict__ lse)
 {
-    using T = AttnTile<D>;
+    using G = Geo<D>;
+    constexpr int NW = 4;
     extern __shared__ __align__(16) uint16_t smem[];
 
-    const int rg = blockIdx.x;
-    const int r = rg / nkv, g = rg % nkv;
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int w = tid >> 6;
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    const int rg = group_id_x();
+    const int r = uni(rg / nkv), g = rg - r * nkv;
+    const int wave = uni(thread_id() >> 6);
+    const int lane = lane_id(), col = lane & 31, half = lane >> 5;
     const int rows = W * group;
-    const bool wave_active = blockIdx.y * 128 + w * 32 < rows;
+    const int wr0 = group_id_y() * 128 + wave * 32;
+    const bool wave_active = wr0 < rows;
 
-    // query row within (r, g): beam * G + head-in-group
-    auto query_row = [&](bool &valid, int &beam) {
-        const int n = blockIdx.y * 128 + w * 32 + (threadIdx.x & 31);
-        valid = n < rows;
-        beam = valid ? n / group : 0;
-        const int head = g * group + (valid ? n % group : 0);
-        return ((size_t)r * W + beam) * nq + head;
-    };
+    // this lane's row (rows past the end duplicate the last row; not stored)
+    const int n = min(wr0 + col, rows - 1);
+    const int beam = n / group, h = n - beam * group;
+    const size_t qrow = ((size_t)r * W + beam) * nq + (size_t)g * group + h;
 
-    bf16x8 qop[D / 16];
-    {
-        bool valid;
-        int beam;
-        const size_t qi = query_row(valid, beam);
-        load_q_operand<D>(qop, q + qi * D, valid);
+    const uint32_t lds_base = (uint32_t)(size_t)(const BGA_LDS char *)smem;
+    const uint32_t rbytes = (uint32_t)(nkv * D * 2);
+    const size_t pofs = ((size_t)r * Lp * nkv + g) * D;
+    const uint64_t kbase = uni64((uint64_t)(size_t)(pk + pofs));
+    const uint64_t vbase = uni64((uint64_t)(size_t)(pv + pofs));
+    const int nkt = (Lp + G::BN - 1) / G::BN;
+    const int nkt_w = wave_active ? nkt : 0;
+
+    Copier<D, NW> cp;
+    cp.init(wave, rbytes);
+    if (nkt > 0) {
+        const int last0 = Lp < G::BN ? Lp - 1 : -1;
+        cp.template issue<false>(lds_base + G::kslot(0), kbase, last0);
+        cp.template issue<true>(lds_base + G::vslot(0), vbase, last0);
     }
+    bf16x8 qop[D / 16];
+    load_q<D>(qop, q + qrow * D);
 
-    const BGA_LDS char *lds = lds_ptr(smem);
-    const uint32_t lds_base = lds_addr(lds);
-    WaveAttn<D> st;
-    st.init(lds);
+    Reads<D> rd;
+    rd.init(lds_base);
+    Wave<D> st;
+    st.reset();
     const float c2 = scale * kLog2e;
-
-    // the row's indices (recomputed where needed: fewer registers live across the scan)
-    const int half = (threadIdx.x & 63) >> 5;
-
-    // ---- suffix segment: this beam's own keys, folded into the same state
-    // (invalid query rows read beam 0's rows, which exist, and are dropped at the end)
-    struct SuffixKey {
-        u32x4 k[D / 16];      // K row: this lane's d-half of every 16-wide d step
-        u32x2 v[D / 32][4];   // V row: the d values this lane accumulates
-    };
-    auto suffix = [&]() {   // after the prefix scan (its registers are free by then)
-        bool valid;
-        int beam;
-        query_row(valid, beam);
-        const size_t sbase = (((size_t)r * W + beam) * Ls_cap * nkv + g) * D;
-        const uint32_t rs = (uint32_t)(nkv * D);
-        for (int j = 0; j < Ls; ++j) {
-            SuffixKey x;
-            const uint16_t *kr = sk + sbase + (size_t)j * rs, *vr = sv + sbase + (size_t)j * rs;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) x.k[ks] = *(const u32x4 *)(kr + ks * 16 + half * 8);
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                for (int rgi = 0; rgi < 4; ++rgi) x.v[b][rgi] = *(const u32x2 *)(vr + b * 32 + rgi * 8 + half * 4);
-            float part = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(x.k[ks][e]), part);
-                    part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(x.k[ks][e]), part);
-                }
-            }
-            const float s = pair_sum(part);
-            const float m_new = fmaxf(st.m, s);
-            const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);   // 0 on the first key (m = -inf)
-            const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
-            st.l = st.l * alpha + (half == 0 ? p : 0.f);
-            st.m = m_new;
-#pragma unroll
-            for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-                for (int rgi = 0; rgi < 4; ++rgi) {
-                    const u32x2 vv = x.v[b][rgi];
-                    st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
-                    st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
-                    st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
-                    st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
-                }
-        }
-    };
+    wait_copies_and_sync();
 
     // ---- prefix segment: MFMA tiles through LDS, shared by the 4 waves
-    const uint32_t row_stride = (uint32_t)(nkv * D);
-    DmaPlan<D, 4> plan;   // 4 waves per workgroup
-    plan.init(w, nthr >> 6);
-    const size_t pbase = (size_t)r * Lp * row_stride + (size_t)g * D;
-    const int nkt = (Lp + AttnTile<D>::BN - 1) / AttnTile<D>::BN;
-    attn_scan<D>(st, plan, lds_base, qop, pk + pbase, pv + pbase, row_stride, 0, Lp, nkt, c2,
-                 [&](int kt) { return (kt + 1) * AttnTile<D>::BN > Lp; }, Lp - 1);
-    if (!wave_active) return;
-    suffix();
-    bool row_valid;
-    int beam;
-    const size_t qrow_idx = query_row(row_valid, beam);
-    st.finish(out + qrow_idx * D, lse ? lse + qrow_idx : nullptr, row_valid, scale);
+    if (nkt > 0)
+        scan<D, NW>(st, rd, cp, qop, lds_base, kbase, vbase, Lp, nkt, nkt_w, Lp - 1, Lp / G::BN, c2, true);
+
+    // ---- suffix segment: this beam's own keys, folded into the same state
+    const size_t sbase = (((size_t)r * W + beam) * Ls_cap * nkv + g) * D;
+    const uint32_t rs = (uint32_t)(nkv * D);
+    for (int j = 0; j < (wave_active ? Ls : 0); ++j) {
+        const uint16_t *kr = sk + sbase + (size_t)j * rs, *vr = sv + sbase + (size_t)j * rs;
+        u32x4 kx[D / 16];
+        u32x2 vx[D / 32][4];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) kx[ks] = *(const u32x4 *)(kr + ks * 16 + half * 8);
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int rgi = 0; rgi < 4; ++rgi) vx[b][rgi] = *(const u32x2 *)(vr + b * 32 + rgi * 8 + half * 4);
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(kx[ks][e]), part);
+                part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(kx[ks][e]), part);
+            }
+        }
+        const float s = pair_sum(part);
+        const float m_new = fmaxf(st.m, s);
+        const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);   // 0 while no key was seen (m = -inf)
+        const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
+        st.l = st.l * alpha + (half == 0 ? p : 0.f);
+        st.m = m_new;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int rgi = 0; rgi < 4; ++rgi) {
+                const u32x2 vv = vx[b][rgi];
+                st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
+                st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
+                st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
+                st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
+            }
+    }
+    if (wave_active) st.finish(out + qrow * D, lse ? lse + qrow : nullptr, wr0 + col < rows, scale);
 }
 
 template <int D>
@@ -139,7 +131,7 @@ static hipError_t launch_decode_d(const uint16_t *q, const uint16_t *pk, const u
 {
     const int group = nq / nkv;
     const int rows = W * group;
-    const size_t smem = AttnTile<D>::SMEM_BYTES;
+    const size_t smem = Geo<D>::SMEM;
     hipError_t e = hipFuncSetAttribute((const void *)shared_prefix_decode_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;

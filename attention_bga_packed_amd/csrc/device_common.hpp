@@ -16,6 +16,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// work-item and workgroup ids straight from the hardware registers (the
+// blockIdx / threadIdx wrappers can end up as out-of-line library calls)
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_workitem_id_x() & 63; }
+__device__ __forceinline__ int group_id_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int group_id_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+
 // bf16 bits -> fp32 (exact)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
