@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel it was measured on and is reported as null once they change.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {
-    "packed_gqa_prefill": ["prefill.hip", "attn_tile.hpp", "device_common.hpp", "internal.hpp"],
-    "shared_prefix_decode": ["decode.hip", "attn_tile.hpp", "device_common.hpp", "internal.hpp"],
+    "packed_gqa_prefill": ["prefill.hip", "attn_core.hpp", "device_common.hpp", "internal.hpp"],
+    "shared_prefix_decode": ["decode.hip", "attn_core.hpp", "device_common.hpp", "internal.hpp"],
     "beam_topk": ["topk.hip", "device_common.hpp", "internal.hpp"],
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
