@@ -49,7 +49,9 @@ constexpr int TK1_WAVES = TK1_THREADS / 64;
 constexpr int TK1_UNROLL = 4;      // 16-byte chunks in flight per thread
 constexpr int TK_LIST = 4096;      // candidate list entries
 constexpr int TK_SAMPLE = 512;     // sampled 8-logit chunks (4096 logits)
-constexpr int TK_WCHUNKS = 1024;   // per wave: chunks with a candidate (stream)
+constexpr int TK_WCAND = 768;      // per wave: candidate entries found in the stream
+constexpr int TK_RING = 128;       // per wave: queued 16-byte chunks holding a candidate
+static_assert(TK1_WAVES * (TK_WCAND + 2 * TK_RING) <= TK_LIST, "candidate regions and rings share the list");
 constexpr int TK2_THREADS = 1024;  // stage 2: one workgroup per request, one beam per thread
 
 __device__ __forceinline__ uint32_t key16(uint32_t b)
@@ -312,7 +314,6 @@ struct Tk1Shared {
     union {
         unsigned long long list[TK_LIST];     // candidates: key << 32 | ~id
         uint16_t sample[TK_SAMPLE * 8];       // sampled keys (before the stream)
-        int32_t chunks[TK1_THREADS / 64][TK_WCHUNKS];   // per wave: chunks holding keys >= t (stream)
     };
     uint32_t whist[TK1_THREADS / 64][256];    // per-wave digit histograms of the sample
     float lmax[TK1_THREADS / 64];
@@ -428,18 +429,63 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         }
         __syncthreads();
         const int nsamp = ns * 8;
-        // expected count of row keys >= the j-th largest sample key: about j * V / nsamp = 2.5k
-        const uint32_t j = (uint32_t)min((long long)nsamp, (5ll * k * nsamp + 2ll * V - 1) / (2ll * V) + 8);
+        // expected count of row keys >= the j-th largest sample key: about j * V / nsamp = 1.5k
+        // (plus a margin of 8 sample ranks)
+        const uint32_t j = (uint32_t)min((long long)nsamp, (3ll * k * nsamp + 2ll * V - 1) / (2ll * V) + 8);
         tkey = sample_select(sh, nsamp, j);
         __syncthreads();   // the sample is dead: the list reuses its memory
     }
     const float tval = tkey > 1u ? key16_value(tkey) : -INFINITY;   // value form of the cut (prefilter)
     __syncthreads();
 
-    // ---- stream: per-lane lazy offset m and fp64 sum of exp(x - m); note chunks with keys >= t
+    // ---- stream: per-lane lazy offset m and fp64 sum of exp(x - m); candidates >= t
+    // A chunk whose maximum reaches t is pushed (data and index) onto the wave's
+    // ring in LDS; whenever 64 are queued the wave takes one per lane, extracts
+    // its keys >= t and appends them to the wave's candidate region. The row is
+    // read once: the candidates come from data already in registers.
     float m = -INFINITY;
     double acc = 0.0;
-    uint32_t wcount = 0;   // chunks this wave noted (wave-uniform)
+    uint32_t rpos = 0;     // ring fill (wave-uniform)
+    uint32_t lcount = 0;   // candidates this wave found (wave-uniform; stored while < TK_WCAND)
+    u32x4 *const ring = (u32x4 *)(sh.list + TK1_WAVES * TK_WCAND) + w * TK_RING;
+    uint32_t *const ring_id = &sh.whist[0][0] + w * TK_RING;
+    unsigned long long *const wlist = sh.list + w * TK_WCAND;
+    auto drain = [&](uint32_t n) {   // the ring's first n <= 64 chunks (wave-uniform n)
+        const bool have = (uint32_t)lane < n;
+        const u32x4 d = have ? ring[lane] : u32x4{0u, 0u, 0u, 0u};
+        const int c = have ? (int)ring_id[lane] : 0;
+        uint32_t hm = 0;   // bit e*2+h: element 2e+h of the chunk is a candidate
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hm |= (bf16_lo(d[e]) >= tval ? 1u : 0u) << (2 * e);
+            hm |= (bf16_hi(d[e]) >= tval ? 1u : 0u) << (2 * e + 1);
+        }
+        // finite logits: value order is key order; ids >= V are padding
+        hm = have ? hm & ((1u << min(8, V - c * 8)) - 1u) : 0u;
+        const uint32_t cnt = (uint32_t)__popc(hm);
+        const uint32_t incl = wave_incl_scan_u32(cnt);
+        const uint32_t tot = (uint32_t)__shfl(incl, 63);
+        uint32_t at = lcount + incl - cnt;
+        while (hm) {
+            const int b = __ffs(hm) - 1;
+            hm &= hm - 1;
+            const uint32_t word = d[b >> 1];
+            const uint32_t key = key16((b & 1) ? (word >> 16) : (word & 0xffffu));
+            const uint32_t id = (uint32_t)(c * 8 + b);
+            if (at < (uint32_t)TK_WCAND) wlist[at] = ((unsigned long long)key << 32) | (0xffffffffu - id);
+            ++at;
+        }
+        lcount += tot;
+        // move the rest of the ring down (same wave: LDS keeps this order)
+        const uint32_t rest = rpos - n;
+        if ((uint32_t)lane < rest) {
+            const u32x4 t = ring[n + lane];
+            const uint32_t ti = ring_id[n + lane];
+            ring[lane] = t;
+            ring_id[lane] = ti;
+        }
+        rpos = rest;
+    };
     // two buffers of chunks: one is reduced while the other is in flight
     auto load_batch = [&](u32x4 (&buf)[TK1_UNROLL], int i0) {
 #pragma unroll
@@ -474,14 +520,18 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             acc += (double)cs;
         }
 #pragma unroll
-        for (int u = 0; u < TK1_UNROLL; ++u) {   // note the chunks that hold keys >= t
+        for (int u = 0; u < TK1_UNROLL; ++u) {   // queue the chunks that hold keys >= t
             const bool hit = cmax[u] >= tval;
             const unsigned long long mask = __ballot(hit);
-            if (mask) {   // wave-uniform; the wave's own region, no atomics
-                const uint32_t pos = wcount + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+            if (mask) {   // wave-uniform; the wave's own ring, no atomics
+                const uint32_t pos = rpos + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                if (hit && pos < (uint32_t)TK_WCHUNKS) sh.chunks[w][pos] = (i0 + u) * TK1_THREADS + tid;
-                wcount += (uint32_t)__popcll(mask);
+                if (hit) {
+                    ring[pos] = raw[u];
+                    ring_id[pos] = (uint32_t)((i0 + u) * TK1_THREADS + tid);
+                }
+                rpos += (uint32_t)__popcll(mask);
+                if (rpos >= 64u) drain(64u);
             }
         }
     };
@@ -491,79 +541,42 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         load_batch(bufa, i0 + 2 * TK1_UNROLL);
         consume(bufb, i0 + TK1_UNROLL);
     }
+    while (rpos > 0u) drain(min(rpos, 64u));
 
-    // ---- candidates: the keys >= t of the noted chunks (read again, from cache)
-    if (lane == 0) sh.wcnt[w] = wcount;
+    // ---- candidates: the waves' regions, compacted into one list
+    if (lane == 0) sh.wcnt[w] = lcount;
     __syncthreads();
-    uint32_t wc[TK1_THREADS / 64], wtot = 0;
+    uint32_t wc[TK1_WAVES], count = 0;
     bool noted_all = true;
 #pragma unroll
-    for (int i = 0; i < TK1_THREADS / 64; ++i) {
+    for (int i = 0; i < TK1_WAVES; ++i) {
         wc[i] = sh.wcnt[i];
-        noted_all = noted_all && wc[i] <= (uint32_t)TK_WCHUNKS;
-        wc[i] = min(wc[i], (uint32_t)TK_WCHUNKS);
-        wtot += wc[i];
+        noted_all = noted_all && wc[i] <= (uint32_t)TK_WCAND;
+        wc[i] = min(wc[i], (uint32_t)TK_WCAND);
+        count += wc[i];
     }
-    constexpr int kPer = TK1_WAVES * TK_WCHUNKS / TK1_THREADS;   // noted chunks per thread, at most
-    int mych[kPer];
+    {
+        constexpr int kPer = TK1_WAVES * TK_WCAND / TK1_THREADS;
+        unsigned long long e[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        // flat index over the waves' regions
-        uint32_t f = (uint32_t)(tid + j * TK1_THREADS), c = 0xffffffffu;
+        for (int j = 0; j < kPer; ++j) {
+            // flat index f over the waves' regions -> (wave, slot)
+            uint32_t f = (uint32_t)(tid + j * TK1_THREADS), src = 0xffffffffu;
 #pragma unroll
-        for (int i = 0; i < TK1_THREADS / 64; ++i) {
-            if (c == 0xffffffffu && f < wc[i]) c = (uint32_t)sh.chunks[i][f];
-            f = f >= wc[i] ? f - wc[i] : 0xffffffffu;
+            for (int i = 0; i < TK1_WAVES; ++i) {
+                if (src == 0xffffffffu && f < wc[i]) src = (uint32_t)(i * TK_WCAND) + f;
+                f = f >= wc[i] ? f - wc[i] : 0xffffffffu;
+            }
+            e[j] = src != 0xffffffffu ? sh.list[src] : 0ull;
         }
-        mych[j] = (int)c;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t f = (uint32_t)(tid + j * TK1_THREADS);
+            if (f < count) sh.list[f] = e[j];
+        }
     }
-    __syncthreads();   // the chunk lists are read: the candidate list takes their memory
-    // The noted chunks in two rounds of 8 per thread: a round's chunks are all in
-    // flight at once (empty slots read chunk 0), candidates are counted, and one
-    // block scan places them (no atomics).
-    uint32_t at_total = 0;
-    auto gather_round = [&](auto round) {
-        constexpr int r = decltype(round)::value;
-        u32x4 craw[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) craw[j] = load_raw<VEC>(x, max(mych[r * 8 + j], 0), V, nchunks);
-        uint32_t hits[8], ncand = 0;   // per chunk: bit e*2+h set for a candidate
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = mych[r * 8 + j];
-            uint32_t hm = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hm |= (bf16_lo(craw[j][e]) >= tval ? 1u : 0u) << (2 * e);
-                hm |= (bf16_hi(craw[j][e]) >= tval ? 1u : 0u) << (2 * e + 1);
-            }
-            // finite logits: value order is key order; drop empty slots and ids >= V
-            const int valid = c < 0 ? 0 : min(8, V - c * 8);
-            hm &= (1u << valid) - 1u;
-            hits[j] = hm;
-            ncand += (uint32_t)__popc(hm);
-        }
-        uint32_t rtotal;
-        uint32_t at = at_total + block_excl_scan(sh.c, ncand, &rtotal);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t hm = hits[j];
-            while (hm) {
-                const int b = __ffs(hm) - 1;
-                hm &= hm - 1;
-                const uint32_t word = craw[j][b >> 1];
-                const uint32_t key = key16((b & 1) ? (word >> 16) : (word & 0xffffu));
-                const uint32_t id = (uint32_t)(mych[r * 8 + j] * 8 + b);
-                if (at < (uint32_t)TK_LIST) sh.list[at] = ((unsigned long long)key << 32) | (0xffffffffu - id);
-                ++at;
-            }
-        }
-        at_total += rtotal;
-    };
-    static_assert(kPer == 16, "two gather rounds of 8 chunks per thread");
-    gather_round(Parity0{});
-    if (wtot > (uint32_t)(8 * TK1_THREADS)) gather_round(Parity1{});   // uniform
-    if (tid == 0) sh.count = at_total;
+    if (tid == 0) sh.count = count;
     __syncthreads();
 
     // ---- the row's log-sum-exp from the lanes' (m, sum)
@@ -595,7 +608,6 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     };
 
     // ---- the cut key kappa, keys above it, keys equal to it
-    const uint32_t count = sh.count;
     uint32_t kappa, above, n_eq;
     int n;
     if (noted_all && count >= k && count <= (uint32_t)TK_LIST) {
