@@ -45,10 +45,10 @@ KERNEL_SOURCES = {
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
 MEASURED_TRAFFIC = {
-    "packed_gqa_prefill": {"fetch_kib": 17769.3, "write_kib": 18016.6, "sources_sha256": "e5669ece78ce00ac"},
-    "shared_prefix_decode": {"fetch_kib": 33430.6, "write_kib": 13600.0, "sources_sha256": "b1c0e5cd5586e8fe"},
-    "beam_topk": {"fetch_kib": 862402.1, "write_kib": 26666.9, "sources_sha256": "7ce159611a4e588b"},
-    "suffix_reorder": {"fetch_kib": 15208.7, "write_kib": 38400.0, "sources_sha256": "0626fecf178d2e73"},
+    "packed_gqa_prefill": {"fetch_kib": 17078.5, "write_kib": 17985.9, "sources_sha256": "16ccb73a23ce28a7"},
+    "shared_prefix_decode": {"fetch_kib": 33464.6, "write_kib": 13600.0, "sources_sha256": "932ae5b6a6ed5d25"},
+    "beam_topk": {"fetch_kib": 572907.1, "write_kib": 21080.0, "sources_sha256": "cb7b5284a6759d9b"},
+    "suffix_reorder": {"fetch_kib": 15192.7, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
 }
 
 
