@@ -437,18 +437,16 @@ struct Wave {
 // nkt; the wave computes tiles [0, nkt_w) only. Keys past `lim` (this lane's
 // last allowed key) are masked in tiles kt >= kt_mask. The caller has issued
 // the copies of tile 0 (K0, V0) and waited for them (wait_copies_and_sync);
-// the state st is empty when `fresh`, else it may already hold keys. When
-// `resident`, nkt <= 2 and tiles [0, nkt) already sit in their slots (a previous
-// scan of the same keys left them there): nothing is copied.
+// the state st is empty when `fresh`, else it may already hold keys.
 template <int D, int NW>
 __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copier<D, NW> &cp, const bf16x8 *qop,
                                      uint32_t lds_base, uint64_t kbase, uint64_t vbase, int kend, int nkt, int nkt_w,
-                                     int lim, int kt_mask, float c2, bool fresh, bool resident = false)
+                                     int lim, int kt_mask, float c2, bool fresh)
 {
     using G = Geo<D>;
     const uint64_t tile_bytes = (uint64_t)G::BN * cp.rbytes;
     auto last_row = [&](int kt) { return kt * G::BN + G::BN > kend ? kend - 1 - kt * G::BN : -1; };
-    if (nkt > 1 && !resident) cp.template issue<false>(lds_base + G::kslot(1), kbase + tile_bytes, last_row(1));
+    if (nkt > 1) cp.template issue<false>(lds_base + G::kslot(1), kbase + tile_bytes, last_row(1));
 
     f32x16 sa[2], sb[2];
     if (nkt_w > 0) {
@@ -467,7 +465,6 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
     // K(kt) and V(kt-1) held.
     auto sync_and_copy = [&](int kt) {
         wait_copies_and_sync();   // K(kt+1), V(kt) landed; K(kt), V(kt-1) no longer read
-        if (resident) return;
         const uint32_t p = (uint32_t)(kt & 1);
         if (kt + 2 < nkt)
             cp.template issue<false>(lds_base + p * G::KBYTES, kbase + (uint64_t)(kt + 2) * tile_bytes,

@@ -19,10 +19,13 @@
 // later ones) and masks only the tiles that reach past its first row's token.
 //
 // Grid = (pairs rounded up to a multiple of 8, row blocks). Pair = (sequence,
-// kv head). The row-block index is reversed, so the longest (last) blocks of
-// every sequence are dispatched first. Consecutive workgroups are dealt
-// round-robin over the 8 XCDs, so the pair index in x, padded to a multiple of
-// 8, keeps every block of one (sequence, kv head) on one XCD and its L2.
+// kv head). Dispatch order over the row blocks: block 0 (one key tile, the
+// shortest) first, then the rest longest first. When the grid exceeds what the
+// GPU holds at once, the block-0 workgroups finish early and free their slots
+// for the overflow, and the long blocks start at once. Consecutive workgroups
+// are dealt round-robin over the 8 XCDs, so the pair index in x, padded to a
+// multiple of 8, keeps every block of one (sequence, kv head) on one XCD and
+// its L2.
 #include "attn_core.hpp"
 #include "internal.hpp"
 
@@ -33,8 +36,7 @@ using namespace core;
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void packed_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ cu, int num_pairs, int blocks_y, bool merge01, int nq, int nkv, int group,
-    float scale,
+    const int32_t *__restrict__ cu, int num_pairs, int blocks_y, int nq, int nkv, int group, float scale,
     uint16_t *__restrict__ out, float *__restrict__ lse)
 {
     using G = Geo<D>;
@@ -47,12 +49,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
     const int seq = uni(pair / nkv), g = pair - seq * nkv;
     const int s0 = cu[seq];
     const int nrows = (cu[seq + 1] - s0) * group;
-    // row block of this workgroup; with merge01 the grid has no block 0: the
-    // workgroup of block 1 takes block 0 afterwards (see below)
-    const int blk = blocks_y - 1 - group_id_y() + (merge01 ? 1 : 0);
-    const bool do_blk = blk * ROWS < nrows;
-    const bool do_blk0 = merge01 && blk == 1 && nrows > 0;   // block 0 exists
-    if (!do_blk && !do_blk0) return;   // uniform over the workgroup
+    // row block of this workgroup: y = 0 -> block 0, y = 1 .. -> blocks_y - 1 down to 1
+    const int y = group_id_y();
+    const int blk = y == 0 ? 0 : blocks_y - y;
+    const int n0 = blk * ROWS;
+    if (n0 >= nrows) return;   // uniform over the workgroup
 
     const int wave = uni(thread_id() >> 6);
     const int lane = lane_id(), col = lane & 31;
@@ -66,40 +67,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
     Reads<D> rd;
     rd.init(lds_base);
 
-    // One row block: rows [n0, n0 + ROWS) of the sequence. Wave-uniform values
-    // come from integer division on the vector ALU, so they are read back from
-    // the first lane to keep the control flow scalar.
-    auto block = [&](int n0, bool resident) {
-        // keys [0, kend) of the sequence; tiles [0, nkt)
-        const int kend = uni((min(n0 + ROWS, nrows) - 1) / group + 1);
-        const int nkt = uni((kend + G::BN - 1) / G::BN);
-        // this wave: rows [wr0, wr_last], tiles [0, nkt_w), masked from tile kt_mask on
-        const int wr0 = n0 + wave * 32;
-        const int wr_last = min(wr0 + 31, nrows - 1);
-        const int nkt_w = uni(wr0 < nrows ? (wr_last / group) / G::BN + 1 : 0);
-        const int kt_mask = uni((wr0 / group + 1) / G::BN);
-        // this lane's row (rows past the end duplicate the last row; not stored)
-        const int n = min(wr0 + col, nrows - 1);
-        const int tok = n / group, h = n - tok * group;
-        const size_t qrow = ((size_t)(s0 + tok) * nq + (size_t)g * group + h);
+    // Rows [n0, n0 + ROWS) of the sequence. Wave-uniform values come from
+    // integer division on the vector ALU, so they are read back from the first
+    // lane to keep the control flow scalar.
+    // keys [0, kend) of the sequence; tiles [0, nkt)
+    const int kend = uni((min(n0 + ROWS, nrows) - 1) / group + 1);
+    const int nkt = uni((kend + G::BN - 1) / G::BN);
+    // this wave: rows [wr0, wr_last], tiles [0, nkt_w), masked from tile kt_mask on
+    const int wr0 = n0 + wave * 32;
+    const int wr_last = min(wr0 + 31, nrows - 1);
+    const int nkt_w = uni(wr0 < nrows ? (wr_last / group) / G::BN + 1 : 0);
+    const int kt_mask = uni((wr0 / group + 1) / G::BN);
+    // this lane's row (rows past the end duplicate the last row; not stored)
+    const int n = min(wr0 + col, nrows - 1);
+    const int tok = n / group, h = n - tok * group;
+    const size_t qrow = ((size_t)(s0 + tok) * nq + (size_t)g * group + h);
 
-        if (!resident) {
-            const int last0 = kend < G::BN ? kend - 1 : -1;
-            cp.template issue<false>(lds_base + G::kslot(0), kbase, last0);
-            cp.template issue<true>(lds_base + G::vslot(0), vbase, last0);
-        }
-        bf16x8 qop[D / 16];
-        load_q<D>(qop, q + qrow * D);
-        wait_copies_and_sync();
-        Wave<D> st;
-        st.reset();
-        scan<D, NW>(st, rd, cp, qop, lds_base, kbase, vbase, kend, nkt, nkt_w, tok, kt_mask, c2, true, resident);
-        if (nkt_w > 0) st.finish(out + qrow * D, lse ? lse + qrow : nullptr, wr0 + col < nrows, scale);
-    };
-    // Block 0 needs keys [0, 64 * nkt0) with nkt0 <= 2; block 1 (group >= 2:
-    // tokens below 128) leaves exactly those tiles in their slots. One loop, so
-    // that the block's code exists once.
-    for (int u = do_blk ? 0 : 1; u < (do_blk0 ? 2 : 1); ++u) block(u == 0 ? blk * ROWS : 0, u == 1 && do_blk);
+    const int last0 = kend < G::BN ? kend - 1 : -1;
+    cp.template issue<false>(lds_base + G::kslot(0), kbase, last0);
+    cp.template issue<true>(lds_base + G::vslot(0), vbase, last0);
+    bf16x8 qop[D / 16];
+    load_q<D>(qop, q + qrow * D);
+    wait_copies_and_sync();
+    Wave<D> st;
+    st.reset();
+    scan<D, NW>(st, rd, cp, qop, lds_base, kbase, vbase, kend, nkt, nkt_w, tok, kt_mask, c2, true);
+    if (nkt_w > 0) st.finish(out + qrow * D, lse ? lse + qrow : nullptr, wr0 + col < nrows, scale);
 }
 
 template <int D, int NW>
@@ -110,18 +103,14 @@ static hipError_t launch_prefill_d(const uint16_t *q, const uint16_t *k, const u
     const int group = nq / nkv;
     const int pairs = num_seqs * nkv;
     const int xdim = (pairs + 7) / 8 * 8;
-    const int blocks = (int)(((int64_t)max_seqlen * group + 32 * NW - 1) / (32 * NW));
-    // for group >= 2, block 0 rides on block 1's workgroup (fewer workgroups;
-    // the whole Prefill-Only grid then fits the GPU at once)
-    const bool merge01 = group >= 2 && blocks >= 2;
-    const int blocks_y = merge01 ? blocks - 1 : blocks;
+    const int blocks_y = (int)(((int64_t)max_seqlen * group + 32 * NW - 1) / (32 * NW));
     const size_t smem = Geo<D>::SMEM;
     const void *kern = (const void *)packed_prefill_kernel<D, NW>;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     dim3 grid(xdim, blocks_y), block(64 * NW);
-    hipLaunchKernelGGL((packed_prefill_kernel<D, NW>), grid, block, smem, stream, q, k, v, cu, pairs, blocks_y, merge01,
-                       nq, nkv, group, scale, out, lse);
+    hipLaunchKernelGGL((packed_prefill_kernel<D, NW>), grid, block, smem, stream, q, k, v, cu, pairs, blocks_y, nq,
+                       nkv, group, scale, out, lse);
     return hipGetLastError();
 }
 
