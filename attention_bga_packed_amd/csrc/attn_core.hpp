@@ -430,13 +430,32 @@ struct Wave {
     }
 };
 
+// The first copies of a scan over keys [0, kend) (tiles [0, nkt), nkt >= 1):
+// K and V of tiles 0 and 1 go into their slots at once, so that the scan's
+// first tiles do not wait for a copy issued after the prologue.
+template <int D, int NW>
+__device__ __forceinline__ void first_copies(const Copier<D, NW> &cp, uint32_t lds_base, uint64_t kbase,
+                                             uint64_t vbase, int kend, int nkt)
+{
+    using G = Geo<D>;
+    const uint64_t tile_bytes = (uint64_t)G::BN * cp.rbytes;
+    const int last0 = kend < G::BN ? kend - 1 : -1;
+    cp.template issue<false>(lds_base + G::kslot(0), kbase, last0);
+    cp.template issue<true>(lds_base + G::vslot(0), vbase, last0);
+    if (nkt > 1) {
+        const int last1 = kend < 2 * G::BN ? kend - 1 - G::BN : -1;
+        cp.template issue<false>(lds_base + G::kslot(1), kbase + tile_bytes, last1);
+        cp.template issue<true>(lds_base + G::vslot(1), vbase + tile_bytes, last1);
+    }
+}
+
 // The blocked scan over keys [0, kend) of one K/V range, shared by the
 // prefill and decode kernels. Tile kt holds keys 64 kt + [0, 64); K/V row `key`
 // lives at byte address kbase / vbase + key * row stride. Every wave of the
 // workgroup calls this (it holds the barriers) with the workgroup's tile count
 // nkt; the wave computes tiles [0, nkt_w) only. Keys past `lim` (this lane's
 // last allowed key) are masked in tiles kt >= kt_mask. The caller has issued
-// the copies of tile 0 (K0, V0) and waited for them (wait_copies_and_sync);
+// first_copies (tiles 0 and 1) and waited for them (wait_copies_and_sync);
 // the state st is empty when `fresh`, else it may already hold keys.
 template <int D, int NW>
 __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copier<D, NW> &cp, const bf16x8 *qop,
@@ -446,7 +465,6 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
     using G = Geo<D>;
     const uint64_t tile_bytes = (uint64_t)G::BN * cp.rbytes;
     auto last_row = [&](int kt) { return kt * G::BN + G::BN > kend ? kend - 1 - kt * G::BN : -1; };
-    if (nkt > 1) cp.template issue<false>(lds_base + G::kslot(1), kbase + tile_bytes, last_row(1));
 
     f32x16 sa[2], sb[2];
     if (nkt_w > 0) {
@@ -462,14 +480,14 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
     }
     // Tile kt: K(kt) and V(kt) sit in slot kt & 1. Every tile starts with a
     // barrier after which K(kt+2) and V(kt+1) are copied into the slots that
-    // K(kt) and V(kt-1) held.
+    // K(kt) and V(kt-1) held (V(1) came with the first copies).
     auto sync_and_copy = [&](int kt) {
         wait_copies_and_sync();   // K(kt+1), V(kt) landed; K(kt), V(kt-1) no longer read
         const uint32_t p = (uint32_t)(kt & 1);
         if (kt + 2 < nkt)
             cp.template issue<false>(lds_base + p * G::KBYTES, kbase + (uint64_t)(kt + 2) * tile_bytes,
                                      last_row(kt + 2));
-        if (kt + 1 < nkt)
+        if (kt >= 1 && kt + 1 < nkt)
             cp.template issue<true>(lds_base + G::vslot(0) + (1 - p) * G::KBYTES,
                                     vbase + (uint64_t)(kt + 1) * tile_bytes, last_row(kt + 1));
     };

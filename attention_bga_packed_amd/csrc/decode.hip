@@ -62,11 +62,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
     Copier<D, NW> cp;
     cp.init(wave, rbytes);
-    if (nkt > 0) {
-        const int last0 = Lp < G::BN ? Lp - 1 : -1;
-        cp.template issue<false>(lds_base + G::kslot(0), kbase, last0);
-        cp.template issue<true>(lds_base + G::vslot(0), vbase, last0);
-    }
+    if (nkt > 0) first_copies<D, NW>(cp, lds_base, kbase, vbase, Lp, nkt);
     bf16x8 qop[D / 16];
     load_q<D>(qop, q + qrow * D);
 

@@ -83,9 +83,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
     const int tok = n / group, h = n - tok * group;
     const size_t qrow = ((size_t)(s0 + tok) * nq + (size_t)g * group + h);
 
-    const int last0 = kend < G::BN ? kend - 1 : -1;
-    cp.template issue<false>(lds_base + G::kslot(0), kbase, last0);
-    cp.template issue<true>(lds_base + G::vslot(0), vbase, last0);
+    first_copies<D, NW>(cp, lds_base, kbase, vbase, kend, nkt);
     bf16x8 qop[D / 16];
     load_q<D>(qop, q + qrow * D);
     wait_copies_and_sync();
