@@ -32,10 +32,13 @@
 //   The lanes' (m, sum) pairs merge into the row's fp32 log-sum-exp.
 // Stage 2 (one workgroup per request): each beam's list is sorted, so only its
 // first min(k_local, k_global) entries can matter and the entries above any
-// threshold form a prefix. A lower bound comes from the first J entries of
-// every beam, prefix lengths from binary searches, the exact cut from a radix
-// select over 32-bit score keys, ties by lower flat index, and a final bitonic
-// sort by (score desc, flat index asc).
+// threshold form a prefix. A lower bound L on the cut comes from the first 8
+// entries of every beam (two radix digits of their k-th largest); every entry
+// >= L goes into an LDS list (a beam whose 8th entry is >= L continues from
+// memory, 64 entries per wave read); a listed entry's place in the output is
+// the number of larger entries (score desc, flat index asc). When too many
+// entries are >= L (many equal scores), the exact cut comes from radix selects
+// over the beams' prefixes instead, ties by lower flat index.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -819,31 +822,48 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 
 // ---- stage 2 ----------------------------------------------------------------
 
+constexpr int TK2_LIST = 2048;     // stage 2: candidates sorted in LDS
+
 struct Tk2Shared {
     TkCommon c;
-    unsigned long long list[1024];                 // k_global <= 1024
+    __align__(16) unsigned long long list[TK2_LIST];   // candidates: key << 32 | ~flat index
     uint32_t whist[TK2_THREADS / 64][256];         // per-wave digit histograms
-    uint32_t count;
+    uint16_t inc[TK2_THREADS];                     // beams whose list continues above the bound
+    uint32_t count, n_inc;
 };
 
-// Radix select of the k-th largest 32-bit key over the keys `each` visits,
-// with a histogram per wave (scores crowd into a few leading digits).
-// *above = keys strictly greater, *equal = keys equal to the result.
-template <typename Each>
-__device__ __forceinline__ uint32_t radix_select32_w(Tk2Shared &sh, Each each, uint32_t k, uint32_t *above,
-                                                     uint32_t *equal)
+// A lower bound on the k-th largest of the keys kv[0, C) of every thread
+// (each thread's keys descending, 0 = no key; at least k keys in all): that
+// key with its low 16 bits cleared. Two 8-bit digit passes of a radix select,
+// one histogram per wave; a thread counts each run of equal digits with one
+// atomic (its keys are sorted, so the keys that match the prefix and share a
+// digit are adjacent). Keys >= the bound number at least k.
+template <int C>
+__device__ __forceinline__ uint32_t lower_bound16(Tk2Shared &sh, const uint32_t (&kv)[C], uint32_t k)
 {
     const int tid = threadIdx.x, w = tid >> 6;
     constexpr int NW = TK2_THREADS / 64;
-    uint32_t prefix = 0, mask = 0, krem = k, abv = 0, eq = 0;
+    uint32_t prefix = 0, mask = 0, krem = k;
 #pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 8 * (3 - pass);
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = 24 - 8 * pass;
         for (int i = tid; i < NW * 256; i += TK2_THREADS) (&sh.whist[0][0])[i] = 0;
         __syncthreads();
-        each([&](uint32_t key) {
-            if ((key & mask) == prefix) atomicAdd(&sh.whist[w][(key >> shift) & 255u], 1u);
-        });
+        uint32_t cur = 0, cnt = 0;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const uint32_t key = kv[j];
+            if (key && (key & mask) == prefix) {
+                const uint32_t d = (key >> shift) & 255u;
+                if (cnt && d != cur) {
+                    atomicAdd(&sh.whist[w][cur], cnt);
+                    cnt = 0;
+                }
+                cur = d;
+                ++cnt;
+            }
+        }
+        if (cnt) atomicAdd(&sh.whist[w][cur], cnt);
         __syncthreads();
         if (tid < 256) {
             uint32_t c = 0;
@@ -853,16 +873,11 @@ __device__ __forceinline__ uint32_t radix_select32_w(Tk2Shared &sh, Each each, u
         }
         __syncthreads();
         select_bin(sh.c, sh.c.hist, krem);
-        const uint32_t bin = sh.c.bcast[0], ab = sh.c.bcast[1];
-        eq = sh.c.bcast[2];
-        __syncthreads();
-        abv += ab;
-        krem -= ab;
-        prefix |= bin << shift;
+        krem -= sh.c.bcast[1];
+        prefix |= sh.c.bcast[0] << shift;
         mask |= 255u << shift;
+        __syncthreads();
     }
-    *above = abv;
-    *equal = eq;
     return prefix;
 }
 
@@ -874,7 +889,7 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
                                                                   float *__restrict__ out_score)
 {
     __shared__ Tk2Shared sh;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = blockIdx.x;
     const int kk = min(k_local, k_global);
     const float *sc = ws_score + (size_t)r * W_in * k_local;
@@ -882,50 +897,79 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
     const int b = tid;                       // one beam per thread (W_in <= 1024)
     const bool has_beam = b < W_in;
     const float *brow = sc + (size_t)(has_beam ? b : 0) * k_local;
-
-    // number of entries j < kk of this beam with key >= t (its list is sorted)
-    auto prefix_ge = [&](uint32_t t) -> int {
-        int lo = 0, hi = kk;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (key32(brow[mid]) >= t) lo = mid + 1; else hi = mid;
-        }
-        return lo;
+    auto entry = [&](uint32_t key, int beam, int j) {
+        return ((unsigned long long)key << 32) | (0xffffffffu - (uint32_t)(beam * k_local + j));
     };
 
-    uint32_t need;
-    int gt_end, eq_end;
-    // Fast path: the first C entries of every beam, all loaded at once. If every
-    // beam's later entries fall below the k-th largest of the loaded keys, the
-    // loaded keys hold the whole answer.
+    // -- a lower bound L on the cut: the k-th largest of the first C entries of
+    // every beam, its low 16 bits cleared (a subset of the candidates holds k
+    // keys >= L, so the k-th largest of all of them is >= L)
     constexpr int C = 8;
     const int cb = min(kk, C);
     uint32_t kv[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) kv[j] = (has_beam && j < cb) ? key32(brow[j]) : 0u;   // 0: nothing (finite keys > 0)
-    bool fast = false;
-    if ((long long)W_in * cb >= (long long)k) {
-        uint32_t above0, eq0;
-        const uint32_t tau = radix_select32_w(sh, [&](auto fn) {
+    uint32_t L = 1u;   // every entry
+    if ((long long)W_in * cb >= (long long)k) L = max(lower_bound16(sh, kv, k), 1u);
+
+    // -- every entry >= L goes into the list: the first C from registers; a
+    // beam whose C-th entry is still >= L continues in memory (its list is
+    // sorted, so its entries >= L form a prefix), read 64 at a time by a wave
+    if (tid == 0) {
+        sh.count = 0;
+        sh.n_inc = 0;
+    }
+    __syncthreads();
+    uint32_t nreg = 0;
 #pragma unroll
-            for (int j = 0; j < C; ++j)
-                if (kv[j]) fn(kv[j]);
-        }, k, &above0, &eq0);
-        const bool complete = !has_beam || cb == kk || kv[cb - 1] < tau;   // later entries <= kv[cb-1]
-        if (__syncthreads_and(complete)) {
-            fast = true;
-            need = k - above0;
-            gt_end = 0;
-            eq_end = 0;
+    for (int j = 0; j < C; ++j) nreg += kv[j] >= L ? 1u : 0u;
+    if (nreg) {
+        uint32_t at = atomicAdd(&sh.count, nreg);
 #pragma unroll
-            for (int j = 0; j < C; ++j) {
-                gt_end += kv[j] > tau;
-                eq_end += kv[j] >= tau;
+        for (int j = 0; j < C; ++j)
+            if (kv[j] >= L) {
+                if (at < (uint32_t)TK2_LIST) sh.list[at] = entry(kv[j], b, j);
+                ++at;
             }
+    }
+    if (has_beam && cb < kk && kv[cb - 1] >= L) sh.inc[atomicAdd(&sh.n_inc, 1u)] = (uint16_t)b;
+    __syncthreads();
+    const int n_inc = (int)sh.n_inc;
+    for (int t = w; t < n_inc; t += TK2_THREADS / 64) {
+        const int bb = sh.inc[t];
+        const float *row = sc + (size_t)bb * k_local;
+        for (int j0 = C; j0 < kk; j0 += 64) {
+            const int j = j0 + lane;
+            const uint32_t key = j < kk ? key32(row[j]) : 0u;
+            const bool take = key >= L;
+            const unsigned long long mask = __ballot(take);
+            const uint32_t cnt = (uint32_t)__popcll(mask);
+            uint32_t base = 0;
+            if (lane == 0 && cnt) base = atomicAdd(&sh.count, cnt);
+            base = (uint32_t)__shfl((int)base, 0);
+            if (take) {
+                const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (pos < (uint32_t)TK2_LIST) sh.list[pos] = entry(key, bb, j);
+            }
+            if (cnt < 64u) break;   // the rest of this beam is below L
         }
     }
-    if (!fast) {
-        // -- lower bound tau: the k-th largest of the first J entries of every beam
+    __syncthreads();
+    const uint32_t n = sh.count;   // >= k
+
+    if (n > (uint32_t)TK2_LIST) {
+        // Many entries at or above L (for example, many equal scores): the
+        // exact cut kappa among the prefixes above a second bound, ties by
+        // lower flat index, then the k chosen entries are sorted.
+        auto prefix_ge = [&](uint32_t t) -> int {   // entries j < kk of this beam with key >= t
+            int lo = 0, hi = kk;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (key32(brow[mid]) >= t) lo = mid + 1; else hi = mid;
+            }
+            return lo;
+        };
         const int J = min(kk, (k_global + W_in - 1) / W_in + 1);
         uint32_t a_, e_;
         const uint32_t tau = radix_select<4>(sh.c, [&](auto fn) {
@@ -933,16 +977,14 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
                 for (int j = 0; j < J; ++j) fn(key32(brow[j]));
         }, k, &a_, &e_);
         const int nb = has_beam ? prefix_ge(tau) : 0;
-
-        // -- exact cut among the prefixes
         uint32_t above, n_eq;
         const uint32_t kappa = radix_select<4>(sh.c, [&](auto fn) {
             for (int j = 0; j < nb; ++j) fn(key32(brow[j]));
         }, k, &above, &n_eq);
-        need = k - above;
+        const uint32_t need = k - above;
         // entries [0, gt_end) are above kappa, [gt_end, eq_end) equal it
-        gt_end = has_beam ? prefix_ge(kappa + 1u) : 0;   // finite scores: kappa < 0xffffffff
-        eq_end = gt_end;
+        const int gt_end = has_beam ? prefix_ge(kappa + 1u) : 0;   // finite scores: kappa < 0xffffffff
+        int eq_end = gt_end;
         if (has_beam) {
             int lo = gt_end, hi = nb;
             while (lo < hi) {
@@ -951,35 +993,64 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
             }
             eq_end = lo;
         }
-    }
-    uint32_t ties_total;
-    const uint32_t tie_base = block_excl_scan(sh.c, (uint32_t)(eq_end - gt_end), &ties_total);
-    int take_ties = 0;
-    if (tie_base < need) take_ties = min(eq_end - gt_end, (int)(need - tie_base));
-
-    const int width = pow2_at_least(k_global);
-    for (int i = tid; i < width; i += TK2_THREADS) sh.list[i] = 0ull;
-    if (tid == 0) sh.count = 0;
-    __syncthreads();
-    const int take = gt_end + take_ties;
-    if (take > 0) {
-        const uint32_t slot0 = atomicAdd(&sh.count, (uint32_t)take);
-        for (int j = 0; j < take; ++j) {
-            const uint32_t f = (uint32_t)(b * k_local + j);
-            sh.list[slot0 + j] = ((unsigned long long)key32(brow[j]) << 32) | (0xffffffffu - f);
+        uint32_t ties_total;
+        const uint32_t tie_base = block_excl_scan(sh.c, (uint32_t)(eq_end - gt_end), &ties_total);
+        int take_ties = 0;
+        if (tie_base < need) take_ties = min(eq_end - gt_end, (int)(need - tie_base));
+        if (tid == 0) sh.count = 0;
+        __syncthreads();
+        const int take = gt_end + take_ties;
+        if (take > 0) {
+            const uint32_t slot0 = atomicAdd(&sh.count, (uint32_t)take);
+            for (int j = 0; j < take; ++j) sh.list[slot0 + j] = entry(key32(brow[j]), b, j);
         }
+        __syncthreads();
     }
-    __syncthreads();
-    bitonic_desc(sh.list, width);
 
-    for (int i = tid; i < k_global; i += TK2_THREADS) {
-        const unsigned long long e = sh.list[i];
+    // -- order: the place of a listed entry is the number of larger entries
+    // (entries are distinct, the flat index being part of them; equal scores
+    // order by the complemented index: lower index first). Every thread reads
+    // the whole list in the same order (LDS broadcasts), without barriers.
+    const int m = (int)min(sh.count, (uint32_t)TK2_LIST);   // >= k
+    auto emit = [&](unsigned long long e, uint32_t place) {
+        if (place >= k) return;
         const uint32_t f = 0xffffffffu - (uint32_t)(e & 0xffffffffu);
         const int parent = (int)(f / (uint32_t)k_local), j = (int)(f % (uint32_t)k_local);
         const size_t src = ((size_t)r * W_in + parent) * k_local + j;
-        out_tok[(size_t)r * k_global + i] = ws_tok[src];
-        out_par[(size_t)r * k_global + i] = parent;
-        out_score[(size_t)r * k_global + i] = ws_score[src];
+        out_tok[(size_t)r * k_global + place] = ws_tok[src];
+        out_par[(size_t)r * k_global + place] = parent;
+        out_score[(size_t)r * k_global + place] = ws_score[src];
+    };
+    // entries [m, m rounded up to 8) read as 0 (below every entry)
+    for (int i = m + tid; i < ((m + 7) & ~7); i += TK2_THREADS) sh.list[i] = 0ull;
+    __syncthreads();
+    const int m8 = (m + 7) & ~7;
+    // place of e and e2 (8 entries per step: four 16-byte reads in flight)
+    auto places = [&](unsigned long long e, unsigned long long e2, bool two, uint32_t &p, uint32_t &p2) {
+        p = 0;
+        p2 = 0;
+        const ulonglong2 *l2 = (const ulonglong2 *)sh.list;
+        for (int j = 0; j < m8 / 2; j += 4) {
+            ulonglong2 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = l2[j + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                p += (x[u].x > e ? 1u : 0u) + (x[u].y > e ? 1u : 0u);
+                if (two) p2 += (x[u].x > e2 ? 1u : 0u) + (x[u].y > e2 ? 1u : 0u);
+            }
+        }
+    };
+    const unsigned long long e0 = tid < m ? sh.list[tid] : ~0ull;
+    uint32_t p0, p1;
+    if (m <= TK2_THREADS) {
+        places(e0, 0ull, false, p0, p1);
+        if (tid < m) emit(e0, p0);
+    } else {
+        const unsigned long long e1 = tid + TK2_THREADS < m ? sh.list[tid + TK2_THREADS] : ~0ull;
+        places(e0, e1, true, p0, p1);
+        if (tid < m) emit(e0, p0);
+        if (tid + TK2_THREADS < m) emit(e1, p1);
     }
 }
 
