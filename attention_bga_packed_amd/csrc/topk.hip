@@ -36,7 +36,8 @@
 // entries of every beam (two radix digits of their k-th largest); every entry
 // >= L goes into an LDS list (a beam whose 8th entry is >= L continues from
 // memory, 64 entries per wave read); a listed entry's place in the output is
-// the number of larger entries (score desc, flat index asc). When too many
+// the number of larger entries (score desc, flat index asc), counted over runs
+// of 64 sorted in registers by binary searches. When too many
 // entries are >= L (many equal scores), the exact cut comes from radix selects
 // over the beams' prefixes instead, ties by lower flat index.
 #include "device_common.hpp"
@@ -826,7 +827,7 @@ constexpr int TK2_LIST = 2048;     // stage 2: candidates sorted in LDS
 
 struct Tk2Shared {
     TkCommon c;
-    __align__(16) unsigned long long list[TK2_LIST];   // candidates: key << 32 | ~flat index
+    unsigned long long list[TK2_LIST];             // candidates: key << 32 | ~flat index
     uint32_t whist[TK2_THREADS / 64][256];         // per-wave digit histograms
     uint16_t inc[TK2_THREADS];                     // beams whose list continues above the bound
     uint32_t count, n_inc;
@@ -1009,48 +1010,55 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
 
     // -- order: the place of a listed entry is the number of larger entries
     // (entries are distinct, the flat index being part of them; equal scores
-    // order by the complemented index: lower index first). Every thread reads
-    // the whole list in the same order (LDS broadcasts), without barriers.
+    // order by the complemented index: lower index first). The list is cut into
+    // runs of 64, each sorted by one wave in registers; an entry's place is
+    // the sum over all runs of their entries above it, found by binary search
+    // (in its own run that is its lane).
     const int m = (int)min(sh.count, (uint32_t)TK2_LIST);   // >= k
-    auto emit = [&](unsigned long long e, uint32_t place) {
-        if (place >= k) return;
-        const uint32_t f = 0xffffffffu - (uint32_t)(e & 0xffffffffu);
-        const int parent = (int)(f / (uint32_t)k_local), j = (int)(f % (uint32_t)k_local);
-        const size_t src = ((size_t)r * W_in + parent) * k_local + j;
-        out_tok[(size_t)r * k_global + place] = ws_tok[src];
-        out_par[(size_t)r * k_global + place] = parent;
-        out_score[(size_t)r * k_global + place] = ws_score[src];
-    };
-    // entries [m, m rounded up to 8) read as 0 (below every entry)
-    for (int i = m + tid; i < ((m + 7) & ~7); i += TK2_THREADS) sh.list[i] = 0ull;
+    const int nrun = (m + 63) / 64;
+    for (int i = m + tid; i < nrun * 64; i += TK2_THREADS) sh.list[i] = 0ull;   // 0: below every entry
     __syncthreads();
-    const int m8 = (m + 7) & ~7;
-    // place of e and e2 (8 entries per step: four 16-byte reads in flight)
-    auto places = [&](unsigned long long e, unsigned long long e2, bool two, uint32_t &p, uint32_t &p2) {
-        p = 0;
-        p2 = 0;
-        const ulonglong2 *l2 = (const ulonglong2 *)sh.list;
-        for (int j = 0; j < m8 / 2; j += 4) {
-            ulonglong2 x[4];
+    for (int q = w; q < nrun; q += TK2_THREADS / 64) {
+        unsigned long long v = sh.list[q * 64 + lane];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) x[u] = l2[j + u];
+        for (int size = 2; size <= 64; size <<= 1)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                p += (x[u].x > e ? 1u : 0u) + (x[u].y > e ? 1u : 0u);
-                if (two) p2 += (x[u].x > e2 ? 1u : 0u) + (x[u].y > e2 ? 1u : 0u);
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t lo = lane_xor((uint32_t)v, stride), hi = lane_xor((uint32_t)(v >> 32), stride);
+                const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+                const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
+                v = take_max ? (v > o ? v : o) : (v < o ? v : o);
+            }
+        sh.list[q * 64 + lane] = v;   // the wave's own run: no other wave reads it before the barrier
+    }
+    __syncthreads();
+    for (int q = w; q < nrun; q += TK2_THREADS / 64) {
+        const unsigned long long e = sh.list[q * 64 + lane];
+        if (e == 0ull) continue;   // padding
+        uint32_t place = 0;
+        for (int r0 = 0; r0 < nrun; r0 += 8) {
+            int pos[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) pos[u] = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1)
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (r0 + u < nrun && sh.list[(r0 + u) * 64 + pos[u] + step - 1] > e) pos[u] += step;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {   // the steps reach 63: a run wholly above e counts 64
+                if (r0 + u < nrun && sh.list[(r0 + u) * 64 + 63] > e) pos[u] = 64;
+                place += (uint32_t)pos[u];
             }
         }
-    };
-    const unsigned long long e0 = tid < m ? sh.list[tid] : ~0ull;
-    uint32_t p0, p1;
-    if (m <= TK2_THREADS) {
-        places(e0, 0ull, false, p0, p1);
-        if (tid < m) emit(e0, p0);
-    } else {
-        const unsigned long long e1 = tid + TK2_THREADS < m ? sh.list[tid + TK2_THREADS] : ~0ull;
-        places(e0, e1, true, p0, p1);
-        if (tid < m) emit(e0, p0);
-        if (tid + TK2_THREADS < m) emit(e1, p1);
+        if (place < k) {
+            const uint32_t f = 0xffffffffu - (uint32_t)(e & 0xffffffffu);
+            const int parent = (int)(f / (uint32_t)k_local), j = (int)(f % (uint32_t)k_local);
+            const size_t src = ((size_t)r * W_in + parent) * k_local + j;
+            out_tok[(size_t)r * k_global + place] = ws_tok[src];
+            out_par[(size_t)r * k_global + place] = parent;
+            out_score[(size_t)r * k_global + place] = ws_score[src];
+        }
     }
 }
 
