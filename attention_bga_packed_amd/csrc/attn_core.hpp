@@ -408,25 +408,45 @@ struct Wave {
         l += psum;
     }
 
-    // Final normalisation and stores for this lane's row: orow = its output row
-    // [D], lse_ptr its fp32 slot (or nullptr). Lanes l and l ^ 32 hold the two
-    // halves of the row.
-    __device__ __forceinline__ void finish(uint16_t *orow, float *lse_ptr, bool store, float scale)
+    // Final normalisation and stores of the wave's 32 rows. This lane's row is
+    // output row `orow_idx` of `out` ([*, D] bf16), stored if `store`; lse_ptr
+    // is its fp32 slot (or nullptr). Lanes l and l ^ 32 hold the two halves of
+    // the row, in 8-byte pieces 16 bytes apart, so storing straight from the
+    // accumulators would write 16 bytes into each of 32 rows per instruction.
+    // Instead the wave writes its bf16 rows into its own LDS region `stage`
+    // (32 rows x D, 16-byte chunks XOR-swizzled by row) and reads them back
+    // row-major: every global store instruction then writes 64 / (D / 8) whole
+    // rows. The region must not be in use by any other wave (the caller
+    // synchronises the workgroup before the first wave writes it).
+    __device__ __forceinline__ void finish(uint16_t *out, uint32_t orow_idx, float *lse_ptr, bool store, float scale,
+                                           uint32_t stage)
     {
-        const int lane = lane_id(), half = lane >> 5;
+        constexpr int CH = D / 8;       // 16-byte chunks per row
+        constexpr int RPI = 64 / CH;    // rows per store instruction
+        const int lane = lane_id(), col = lane & 31, half = lane >> 5;
         const float lt = pair_sum(l);
         const float inv = 1.f / lt;
-        if (!store) return;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = b * 32 + rg * 8 + half * 4;
+                const int c = b * 4 + rg;   // chunk of d0 = c * 8 + half * 4
                 const u32x2 val = {pack_bf16x2(o[b][rg * 4 + 0] * inv, o[b][rg * 4 + 1] * inv),
                                    pack_bf16x2(o[b][rg * 4 + 2] * inv, o[b][rg * 4 + 3] * inv)};
-                *(u32x2 *)(orow + d0) = val;
+                const uint32_t a = stage + (uint32_t)(col * G::ROWB + ((c ^ (col & (CH - 1))) << 4) + half * 8);
+                *(BGA_LDS u32x2 *)(size_t)a = val;
             }
-        if (half == 0 && lse_ptr) *lse_ptr = m * scale + __logf(lt);
+        if (half == 0 && lse_ptr && store) *lse_ptr = m * scale + __logf(lt);
+        const int c = lane % CH;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int r = i * RPI + lane / CH;
+            const uint32_t ri = (uint32_t)__shfl((int)orow_idx, r);
+            const bool ok = __shfl((int)store, r) != 0;
+            const u32x4 val =
+                *(const BGA_LDS u32x4 *)(size_t)(stage + (uint32_t)(r * G::ROWB + ((c ^ (r & (CH - 1))) << 4)));
+            if (ok) __builtin_nontemporal_store(val, (u32x4 *)(out + (size_t)ri * D + c * 8));
+        }
     }
 };
 

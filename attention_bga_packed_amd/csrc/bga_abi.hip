@@ -47,6 +47,7 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
     if (!heads_ok(num_q_heads, num_kv_heads)) return BGA_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || max_seqlen > BGA_MAX_SEQLEN) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)total_tokens * num_q_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // output row index
     if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
     if (!cu_seqlens) return BGA_ERR_NULL;
     if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return BGA_OK;
@@ -78,6 +79,7 @@ bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k,
     if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX || prefix_len > BGA_MAX_SEQLEN)
         return BGA_ERR_UNSUPPORTED;
     if ((int64_t)num_requests * num_kv_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * beam_width * num_q_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // output row index
     if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
     if (num_requests == 0 || beam_width == 0) return BGA_OK;
     if (!q || !out) return BGA_ERR_NULL;

@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
                 st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
             }
     }
-    if (wave_active) st.finish(out + qrow * D, lse ? lse + qrow : nullptr, wr0 + col < rows, scale);
+    __syncthreads();   // every wave is done with the prefix slots: they stage the output rows now
+    if (wave_active)
+        st.finish(out, (uint32_t)qrow, lse ? lse + qrow : nullptr, wr0 + col < rows, scale,
+                  lds_base + (uint32_t)(wave * 32 * G::ROWB));
 }
 
 template <int D>

@@ -90,7 +90,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
     Wave<D> st;
     st.reset();
     scan<D, NW>(st, rd, cp, qop, lds_base, kbase, vbase, kend, nkt, nkt_w, tok, kt_mask, c2, true);
-    if (nkt_w > 0) st.finish(out + qrow * D, lse ? lse + qrow : nullptr, wr0 + col < nrows, scale);
+    __syncthreads();   // every wave is done with the K/V slots: they stage the output rows now
+    if (nkt_w > 0)
+        st.finish(out, (uint32_t)qrow, lse ? lse + qrow : nullptr, wr0 + col < nrows, scale,
+                  lds_base + (uint32_t)(wave * 32 * G::ROWB));
 }
 
 template <int D, int NW>

@@ -78,8 +78,8 @@ typedef enum {
  *   lse      [T, num_q_heads] fp32, natural-log log-sum-exp of the scaled
  *            scores, or NULL.
  * Supported: head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 with group
- * <= BGA_MAX_GROUP; num_seqs <= 65535. q, k, v, out 16-byte aligned; lse and
- * cu_seqlens 4-byte aligned.
+ * <= BGA_MAX_GROUP; num_seqs <= 65535; total_tokens * num_q_heads < 2^31. q, k,
+ * v, out 16-byte aligned; lse and cu_seqlens 4-byte aligned.
  */
 bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bga_bf16 *v,
                                   const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
@@ -103,7 +103,8 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
  *   lse        [R, W, num_q_heads] fp32 natural-log log-sum-exp, or NULL
  * Requires prefix_len + suffix_len >= 1, 0 <= suffix_len <= suffix_cap <=
  * BGA_MAX_SUFFIX, W <= BGA_MAX_BEAMS, head_dim in {64, 128}, group <=
- * BGA_MAX_GROUP; suffix pointers may be NULL only when suffix_len == 0.
+ * BGA_MAX_GROUP, R * W * num_q_heads < 2^31; suffix pointers may be NULL only
+ * when suffix_len == 0.
  * q, prefix, suffix and out 16-byte aligned; lse 4-byte aligned.
  */
 bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k, const bga_bf16 *prefix_v,
