@@ -45,10 +45,10 @@ KERNEL_SOURCES = {
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
 MEASURED_TRAFFIC = {
-    "packed_gqa_prefill": {"fetch_kib": 17078.5, "write_kib": 17985.9, "sources_sha256": "16ccb73a23ce28a7"},
-    "shared_prefix_decode": {"fetch_kib": 33464.6, "write_kib": 13600.0, "sources_sha256": "932ae5b6a6ed5d25"},
-    "beam_topk": {"fetch_kib": 572907.1, "write_kib": 21080.0, "sources_sha256": "cb7b5284a6759d9b"},
-    "suffix_reorder": {"fetch_kib": 15192.7, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
+    "packed_gqa_prefill": {"fetch_kib": 17195.6, "write_kib": 17972.2, "sources_sha256": "80e2389ca9054dc7"},
+    "shared_prefix_decode": {"fetch_kib": 33476.7, "write_kib": 13600.0, "sources_sha256": "ee8f721919aeb91c"},
+    "beam_topk": {"fetch_kib": 572350.3, "write_kib": 21052.2, "sources_sha256": "e4aa3a83dfef91e6"},
+    "suffix_reorder": {"fetch_kib": 15191.9, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
 }
 
 
