@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget for the oracle baseline sample (0 disables it)")
+    ap.add_argument("--only", choices=["long_prefill", "long_prefill_1024", "short_decode"], default=None,
+                    help="instead of the step, time one other configuration by itself (its kernel launched back "
+                         "to back) and print a JSON line for it")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size dispatch "
                          "for calibrating the FETCH_SIZE / WRITE_SIZE counters)")
@@ -98,6 +101,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        print(json.dumps(only_config(args, dev)), flush=True)
+        return
 
     # ---------------- inputs (resident in HBM before timing)
     pcfg = wl.CONFIGS["prefill_only"]
@@ -281,6 +287,100 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def timed_launches(fn, n, warmup):
+    """Average duration (ms) of n back-to-back calls fn(i), measured with HIP events on the launching stream
+    behind a spin gate (so the host's launch overhead is not counted)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
+    host = time.perf_counter() - t0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(1 << 20)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gate = int((1 << 20) / max(a.elapsed_time(b), 1e-3) * max(3.0 * host * 1e3, 2.0))
+    torch.cuda._sleep(gate)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def only_config(args, dev):
+    """One configuration other than the step's, timed by itself (--only)."""
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import workloads as wl
+
+    name, K, W0 = args.only, max(args.steps, 1), max(args.warmup, 1)
+    cfg = wl.CONFIGS[name]
+    rec = {"metric": "attention TFLOPS & %bf16 MFMA peak (prefill); GB/s & %HBM peak (beam decode)",
+           "n_gpus": 1, "steps": K, "warmup": W0, "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) Q/K/V)", "vs_baseline": None}
+    if cfg["kind"] == "prefill":
+        lengths = wl.prefill_lengths(cfg)
+        # input sets rotated between launches: together larger than the 256 MB Infinity Cache
+        nsets = 2 if name == "long_prefill_1024" else 3
+        cases = [wl.make_prefill_case(lengths, cfg["nq"], cfg["nkv"], cfg["d"], cfg["seed"] * 1000 + i, dev)
+                 for i in range(nsets)]
+        cu = torch.from_numpy(cases[0].cu_seqlens).to(dev)
+        out = torch.empty_like(cases[0].q)
+        lse = torch.empty(cases[0].q.shape[:2], dtype=torch.float32, device=dev)
+        ms = timed_launches(lambda i: bga.packed_gqa_prefill(cases[i % nsets].q, cases[i % nsets].k, cases[i % nsets].v,
+                                                             cu, max(lengths), out=out, lse=lse), K, W0)
+        flops = wl.prefill_flops(lengths, cfg["nq"], cfg["d"])
+        t = sum(lengths)
+        hbm = t * (2 * cfg["nq"] + 2 * cfg["nkv"]) * cfg["d"] * 2 + t * cfg["nq"] * 4
+        tf = flops / (ms * 1e-3) / 1e12
+        rec.update({"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+                    "config": {"workload": name, "sequences": len(lengths), "total_tokens": t,
+                               "max_len": max(lengths), "num_q_heads": cfg["nq"], "num_kv_heads": cfg["nkv"],
+                               "head_dim": cfg["d"], "input_sets": nsets},
+                    "roofline": {"bound": "mfma" if flops / hbm > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm",
+                                 "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                 "algorithmic_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2),
+                                 "hbm_bytes_per_launch": hbm,
+                                 "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}})
+        return rec
+    # decode: every suffix length of the configuration, several input sets rotated
+    nsets = 4
+    cases = [wl.make_decode_case(cfg["r"], cfg["w"], cfg["lp"], cfg["ls_cap"], cfg["nq"], cfg["nkv"], cfg["d"],
+                                 cfg["seed"] * 1000 + i, dev) for i in range(nsets)]
+    out = torch.empty_like(cases[0].q)
+    lse = torch.empty(cases[0].q.shape[:3], dtype=torch.float32, device=dev)
+    per, tot_b, tot_ms = [], 0, 0.0
+    for ls in range(1, cfg["steps"] + 1):
+        ms = timed_launches(lambda i: bga.shared_prefix_decode(cases[i % nsets].q, cases[i % nsets].prefix_k,
+                                                               cases[i % nsets].prefix_v, cases[i % nsets].suffix_k,
+                                                               cases[i % nsets].suffix_v, ls, out=out, lse=lse), K, W0)
+        b = wl.decode_bytes(cfg["r"], cfg["w"], cfg["nq"], cfg["nkv"], cfg["lp"], ls, cfg["d"])
+        per.append(round(ms * 1e3, 2))
+        tot_b += b
+        tot_ms += ms
+    gbs = tot_b / (tot_ms * 1e-3) / 1e9
+    rec.update({"value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(tot_ms / cfg["steps"], 4),
+                "decode_us_per_step": per,
+                "config": {"workload": name, "requests": cfg["r"], "beams": cfg["w"], "prefix_len": cfg["lp"],
+                           "decode_steps": cfg["steps"], "num_q_heads": cfg["nq"], "num_kv_heads": cfg["nkv"],
+                           "head_dim": cfg["d"], "input_sets": nsets},
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                             "algorithmic_per_launch": tot_b // cfg["steps"],
+                             "avg_launch_us": round(tot_ms / cfg["steps"] * 1e3, 2)}})
+    return rec
 
 
 def cpu_baseline(case, flops, seconds):
