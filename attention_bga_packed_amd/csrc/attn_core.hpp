@@ -477,10 +477,15 @@ __device__ __forceinline__ void first_copies(const Copier<D, NW> &cp, uint32_t l
 // last allowed key) are masked in tiles kt >= kt_mask. The caller has issued
 // first_copies (tiles 0 and 1) and waited for them (wait_copies_and_sync);
 // the state st is empty when `fresh`, else it may already hold keys.
-template <int D, int NW>
+// extra(kt) runs in every tile step, after that step's barrier and copies.
+struct NoExtra {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int D, int NW, typename Extra = NoExtra>
 __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copier<D, NW> &cp, const bf16x8 *qop,
                                      uint32_t lds_base, uint64_t kbase, uint64_t vbase, int kend, int nkt, int nkt_w,
-                                     int lim, int kt_mask, float c2, bool fresh)
+                                     int lim, int kt_mask, float c2, bool fresh, Extra extra = Extra())
 {
     using G = Geo<D>;
     const uint64_t tile_bytes = (uint64_t)G::BN * cp.rbytes;
@@ -510,6 +515,7 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
         if (kt >= 1 && kt + 1 < nkt)
             cp.template issue<true>(lds_base + G::vslot(0) + (1 - p) * G::KBYTES,
                                     vbase + (uint64_t)(kt + 1) * tile_bytes, last_row(kt + 1));
+        extra(kt);
     };
     // all but the wave's last tile: exponentials and P*V of tile kt, scores of kt+1
     auto step = [&](int kt, auto parity, f32x16(&sc)[2], f32x16(&sn)[2]) {

@@ -73,49 +73,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const float c2 = scale * kLog2e;
     wait_copies_and_sync();
 
+    // Suffix rows. For one position j the suffix K (or V) rows of this
+    // workgroup's beams lie a constant stride apart, so they are copied like a
+    // key tile: global -> LDS with the copier, into the K/V slots (the K chunk
+    // swizzle for both), up to 64 beams per slot. With at most 64 beams a
+    // position takes one K and one V slot and two positions are in flight:
+    // position 0 goes into the slots that the last prompt tile leaves idle,
+    // during that tile; each later one is copied as soon as the position two
+    // before it has been read. With more beams a position takes all four
+    // slots and positions are copied one at a time.
+    const int bfirst = uni(group_id_y() * 128 / group);
+    const int nbeam = uni(min(group_id_y() * 128 + 127, rows - 1) / group) - bfirst + 1;   // 1 .. 128
+    const int tp = nbeam > G::BN ? 2 : 1;   // 64-row slots per position (K, and as many for V)
+    const uint32_t sstride = (uint32_t)(Ls_cap * nkv * D * 2);   // bytes from one beam's row to the next
+    const uint32_t pos_bytes = (uint32_t)(nkv * D * 2);          // bytes from one position to the next
+    const size_t sofs = (((size_t)r * W + bfirst) * Ls_cap * nkv + g) * D;
+    const uint64_t skb = uni64((uint64_t)(size_t)(sk + sofs));
+    const uint64_t svb = uni64((uint64_t)(size_t)(sv + sofs));
+    Copier<D, NW> scp;
+    scp.init(wave, sstride);
+    auto issue_pos = [&](int j, int set) {   // position j into slot set `set` (tp == 1) or all slots
+        for (int t = 0; t < tp; ++t) {
+            const int nrow = min(G::BN, nbeam - t * G::BN);
+            const uint64_t off = (uint64_t)j * pos_bytes + (uint64_t)t * G::BN * sstride;
+            const int slot = tp == 1 ? set : t;
+            scp.template issue<false>(lds_base + G::kslot(slot), skb + off, nrow < G::BN ? nrow - 1 : -1);
+            scp.template issue<false>(lds_base + G::vslot(slot), svb + off, nrow < G::BN ? nrow - 1 : -1);
+        }
+    };
+    // slot set of the last prompt tile's K/V; position 0 goes into the other one
+    const int s0 = tp == 1 ? (nkt > 0 ? 1 - ((nkt - 1) & 1) : 0) : 0;
+    const bool pos0_in_scan = tp == 1 && Ls > 0 && nkt > 0;
+    auto extra = [&](int kt) {
+        if (pos0_in_scan && kt == nkt - 1) issue_pos(0, s0);
+    };
+
     // ---- prefix segment: MFMA tiles through LDS, shared by the 4 waves
     if (nkt > 0)
-        scan<D, NW>(st, rd, cp, qop, lds_base, kbase, vbase, Lp, nkt, nkt_w, Lp - 1, Lp / G::BN, c2, true);
+        scan<D, NW>(st, rd, cp, qop, lds_base, kbase, vbase, Lp, nkt, nkt_w, Lp - 1, Lp / G::BN, c2, true, extra);
 
     // ---- suffix segment: this beam's own keys, folded into the same state
-    const size_t sbase = (((size_t)r * W + beam) * Ls_cap * nkv + g) * D;
-    const uint32_t rs = (uint32_t)(nkv * D);
-    for (int j = 0; j < (wave_active ? Ls : 0); ++j) {
-        const uint16_t *kr = sk + sbase + (size_t)j * rs, *vr = sv + sbase + (size_t)j * rs;
-        u32x4 kx[D / 16];
-        u32x2 vx[D / 32][4];
+    __syncthreads();   // every wave is done with the last prompt tile's slots
+    if (Ls > 0 && !pos0_in_scan) issue_pos(0, s0);
+    if (tp == 1 && Ls > 1) issue_pos(1, 1 - s0);
+    constexpr int kPerPos = 2 * Copier<D, NW>::N;   // copies of one position per wave (tp == 1)
+    static_assert(kPerPos < 16, "vmcnt immediate");
+    const int brow = beam - bfirst, bt = brow >> 6, rt = brow & (G::BN - 1);
+    const int sw = G::swk(rt);
+    for (int j = 0; j < Ls; ++j) {
+        const int set = (j & 1) ? 1 - s0 : s0;   // slot set of position j (tp == 1; wave-uniform)
+        const int rset = tp == 1 ? set : bt;      // the slot this lane's beam row is in
+        if (tp == 1 && j + 1 < Ls)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | kPerPos);   // position j landed (j + 1 may be in flight)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        if (wave_active) {
+            const uint32_t kb = lds_base + G::kslot(rset) + (uint32_t)(rt * G::ROWB);
+            const uint32_t vb = lds_base + G::vslot(rset) + (uint32_t)(rt * G::ROWB);
+            u32x4 kx[D / 16];
+            u32x2 vx[D / 32][4];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) kx[ks] = *(const u32x4 *)(kr + ks * 16 + half * 8);
+            for (int ks = 0; ks < D / 16; ++ks)
+                kx[ks] = *(const BGA_LDS u32x4 *)(size_t)(kb + (uint32_t)(((ks * 2 + half) ^ sw) << 4));
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+            for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-            for (int rgi = 0; rgi < 4; ++rgi) vx[b][rgi] = *(const u32x2 *)(vr + b * 32 + rgi * 8 + half * 4);
-        float part = 0.f;
+                for (int rgi = 0; rgi < 4; ++rgi)
+                    vx[b][rgi] =
+                        *(const BGA_LDS u32x2 *)(size_t)(vb + (uint32_t)((((b * 4 + rgi) ^ sw) << 4) + half * 8));
+            float part = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const u32x4 qv = __builtin_bit_cast(u32x4, qop[ks]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(kx[ks][e]), part);
-                part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(kx[ks][e]), part);
+                for (int e = 0; e < 4; ++e) {
+                    part = __builtin_fmaf(bf16_lo(qv[e]), bf16_lo(kx[ks][e]), part);
+                    part = __builtin_fmaf(bf16_hi(qv[e]), bf16_hi(kx[ks][e]), part);
+                }
+            }
+            const float s = pair_sum(part);
+            const float m_new = fmaxf(st.m, s);
+            const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);   // 0 while no key was seen (m = -inf)
+            const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
+            st.l = st.l * alpha + (half == 0 ? p : 0.f);
+            st.m = m_new;
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+                for (int rgi = 0; rgi < 4; ++rgi) {
+                    const u32x2 vv = vx[b][rgi];
+                    st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
+                    st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
+                    st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
+                    st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
+                }
+        }
+        if (j + 1 < Ls) {
+            __syncthreads();   // every wave has read position j's slots
+            if (tp == 1) {
+                if (j + 2 < Ls) issue_pos(j + 2, set);
+            } else {
+                issue_pos(j + 1, 0);
             }
         }
-        const float s = pair_sum(part);
-        const float m_new = fmaxf(st.m, s);
-        const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);   // 0 while no key was seen (m = -inf)
-        const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
-        st.l = st.l * alpha + (half == 0 ? p : 0.f);
-        st.m = m_new;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int rgi = 0; rgi < 4; ++rgi) {
-                const u32x2 vv = vx[b][rgi];
-                st.o[b][rgi * 4 + 0] = __builtin_fmaf(st.o[b][rgi * 4 + 0], alpha, p * bf16_lo(vv[0]));
-                st.o[b][rgi * 4 + 1] = __builtin_fmaf(st.o[b][rgi * 4 + 1], alpha, p * bf16_hi(vv[0]));
-                st.o[b][rgi * 4 + 2] = __builtin_fmaf(st.o[b][rgi * 4 + 2], alpha, p * bf16_lo(vv[1]));
-                st.o[b][rgi * 4 + 3] = __builtin_fmaf(st.o[b][rgi * 4 + 3], alpha, p * bf16_hi(vv[1]));
-            }
     }
     __syncthreads();   // every wave is done with the prefix slots: they stage the output rows now
     if (wave_active)

@@ -57,6 +57,8 @@ def test_long_beam_decode_config_sampled(ls):
     (3, 70, 130, 3, 4, 14, 2, 64),   # W*G not a multiple of 128
     (2, 9, 64, 2, 2, 16, 1, 128),    # group 16
     (1, 33, 1, 1, 1, 3, 1, 64),      # prefix of one token
+    (2, 100, 70, 3, 4, 8, 8, 64),    # group 1: up to 128 beams per workgroup (suffix rows in two slots)
+    (1, 130, 64, 2, 2, 4, 4, 128),   # group 1, a full and a ragged workgroup, one prompt tile
 ])
 def test_decode_edge_shapes(r, w, lp, ls, cap, nq, nkv, d):
     c = wl.make_decode_case(r, w, lp, cap, nq, nkv, d, seed=r * 1000 + w + lp)
