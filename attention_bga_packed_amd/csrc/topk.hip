@@ -15,7 +15,8 @@
 //
 // Stage 1 (one 256-thread workgroup per beam row, several per CU) reads the
 // row from HBM once:
-//   threshold: the keys of an evenly strided sample of 4096 logits give a
+//   threshold: the keys of a sample of 4096 logits (64 runs of 64, spread
+//     evenly over the row) give a
 //     cut t whose expected count in the row is about 2.5k (k = k_local); for
 //     rows that fit the candidate list whole, t takes every element.
 //   stream: every lane keeps a running offset m (its largest logit so far,
@@ -421,9 +422,13 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     // ---- threshold key t from a strided sample (t = 1: every element)
     uint32_t tkey = 1u;
     if (V > TK_LIST) {
+        // whole 8-chunk (128-byte) groups spread evenly over the row: the sample
+        // costs its own size in traffic, not one cache line per chunk
         const int ns = min(nchunks, TK_SAMPLE);
+        const int ngrp = nchunks >> 3, sgrp = ns >> 3;
         for (int i = tid; i < ns; i += TK1_THREADS) {
-            const int c = (int)(((long long)i * nchunks) / ns);
+            const int c = sgrp > 0 && (i >> 3) < sgrp ? (int)(((long long)(i >> 3) * ngrp) / sgrp) * 8 + (i & 7)
+                                                      : (int)(((long long)i * nchunks) / ns);
             const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
