@@ -45,10 +45,10 @@ KERNEL_SOURCES = {
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
 MEASURED_TRAFFIC = {
-    "packed_gqa_prefill": {"fetch_kib": 17195.6, "write_kib": 17972.2, "sources_sha256": "80e2389ca9054dc7"},
-    "shared_prefix_decode": {"fetch_kib": 33476.7, "write_kib": 13600.0, "sources_sha256": "ee8f721919aeb91c"},
-    "beam_topk": {"fetch_kib": 572350.3, "write_kib": 21052.2, "sources_sha256": "e4aa3a83dfef91e6"},
-    "suffix_reorder": {"fetch_kib": 15191.9, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
+    "packed_gqa_prefill": {"fetch_kib": 17173.7, "write_kib": 17972.2, "sources_sha256": "63a7f5e4487d387a"},
+    "shared_prefix_decode": {"fetch_kib": 34130.7, "write_kib": 14944.0, "sources_sha256": "35756fe22eeed70b"},
+    "beam_topk": {"fetch_kib": 486908.0, "write_kib": 20418.7, "sources_sha256": "e3c0a399665c05a1"},
+    "suffix_reorder": {"fetch_kib": 15192.4, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
 }
 
 
@@ -239,8 +239,19 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel),
                 "algorithmic_per_launch": per_launch, "avg_launch_us": round(ms * 1e3, 2)}
 
+    # The prefill layer's roofline follows from its arithmetic intensity: below the ridge
+    # (2500 TFLOP/s / 8000 GB/s = 312.5 FLOP/B) HBM bounds it, above it the matrix cores do.
+    pre_bytes = wl.prefill_bytes(lengths, pcfg["nq"], pcfg["nkv"], pcfg["d"])
+    pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
+    if pre_flops / pre_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        pre_roof = roof("packed_gqa_prefill", "hbm", pre_gbs, PEAK_HBM_GBS, "GB/s", pre_bytes, pre_ms)
+    else:
+        pre_roof = roof("packed_gqa_prefill", "mfma", pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre_flops, pre_ms)
+    pre_roof.update({"flop_per_byte": round(pre_flops / pre_bytes, 1), "tflops": round(pre_tflops, 2),
+                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "gbs": round(pre_gbs, 1),
+                     "hbm_frac": round(pre_gbs / PEAK_HBM_GBS, 4)})
     rooflines = {
-        "packed_gqa_prefill": roof("packed_gqa_prefill", "mfma", pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre_flops, pre_ms),
+        "packed_gqa_prefill": pre_roof,
         "shared_prefix_decode": roof("shared_prefix_decode", "hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_bytes)),
                                      float(np.mean(dec_ms))),
         "beam_topk": roof("beam_topk", "hbm", top_gbs, PEAK_HBM_GBS, "GB/s", top_bytes, top_ms),
@@ -342,18 +353,23 @@ def only_config(args, dev):
                                                              cu, max(lengths), out=out, lse=lse), K, W0)
         flops = wl.prefill_flops(lengths, cfg["nq"], cfg["d"])
         t = sum(lengths)
-        hbm = t * (2 * cfg["nq"] + 2 * cfg["nkv"]) * cfg["d"] * 2 + t * cfg["nq"] * 4
+        hbm = wl.prefill_bytes(lengths, cfg["nq"], cfg["nkv"], cfg["d"])
         tf = flops / (ms * 1e-3) / 1e12
+        gbs = hbm / (ms * 1e-3) / 1e9
+        if flops / hbm < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+            roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_per_launch": hbm}
+        else:
+            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_BF16_TFLOPS, 4), "algorithmic_per_launch": flops}
+        roof.update({"traffic": None, "avg_launch_us": round(ms * 1e3, 2), "flop_per_byte": round(flops / hbm, 1),
+                     "tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "gbs": round(gbs, 1),
+                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
         rec.update({"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
                     "config": {"workload": name, "sequences": len(lengths), "total_tokens": t,
                                "max_len": max(lengths), "num_q_heads": cfg["nq"], "num_kv_heads": cfg["nkv"],
                                "head_dim": cfg["d"], "input_sets": nsets},
-                    "roofline": {"bound": "mfma" if flops / hbm > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm",
-                                 "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                                 "algorithmic_per_launch": flops, "avg_launch_us": round(ms * 1e3, 2),
-                                 "hbm_bytes_per_launch": hbm,
-                                 "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}})
+                    "roofline": roof})
         return rec
     # decode: every suffix length of the configuration, several input sets rotated
     nsets = 4

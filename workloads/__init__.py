@@ -25,6 +25,7 @@ from .generators import (  # noqa: F401
 from .counts import (  # noqa: F401
     causal_pairs,
     prefill_flops,
+    prefill_bytes,
     decode_flops,
     decode_bytes,
     reorder_bytes,

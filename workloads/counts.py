@@ -26,6 +26,12 @@ def prefill_flops(lengths, nq: int, d: int) -> int:
     return 4 * d * nq * causal_pairs(lengths)
 
 
+def prefill_bytes(lengths, nq: int, nkv: int, d: int, with_lse: bool = True) -> int:
+    """Algorithmic HBM bytes of one packed prefill: Q, K, V read once, O (and LSE) written once."""
+    t = int(sum(lengths))
+    return t * (2 * nq + 2 * nkv) * d * 2 + (t * nq * 4 if with_lse else 0)
+
+
 def decode_flops(r: int, w: int, nq: int, lp: int, ls: int, d: int) -> int:
     return 4 * r * w * nq * (lp + ls) * d
 
