@@ -564,11 +564,16 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         wc[i] = min(wc[i], (uint32_t)TK_WCAND);
         count += wc[i];
     }
+    // the same value in every thread: kept in a scalar register, so that the
+    // loops below skip whole iterations past the listed entries
+    const int ucnt = __builtin_amdgcn_readfirstlane((int)count);
     {
         constexpr int kPer = TK1_WAVES * TK_WCAND / TK1_THREADS;
         unsigned long long e[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
+            e[j] = 0ull;
+            if (j * TK1_THREADS >= ucnt) continue;
             // flat index f over the waves' regions -> (wave, slot)
             uint32_t f = (uint32_t)(tid + j * TK1_THREADS), src = 0xffffffffu;
 #pragma unroll
@@ -582,7 +587,7 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const uint32_t f = (uint32_t)(tid + j * TK1_THREADS);
-            if (f < count) sh.list[f] = e[j];
+            if (j * TK1_THREADS < ucnt && f < count) sh.list[f] = e[j];
         }
     }
     if (tid == 0) sh.count = count;
@@ -628,6 +633,8 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         bool wide = false;
 #pragma unroll
         for (int j = 0; j < kPerT; ++j) {
+            ent[j] = 0ull;
+            if (j * TK1_THREADS >= ucnt) continue;
             const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
             ent[j] = idx < count ? sh.list[idx] : 0ull;
             wide = wide || (idx < count && (uint32_t)(ent[j] >> 32) - tkey >= 1024u);
@@ -636,11 +643,13 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             uint32_t *hist = &sh.whist[0][0];                     // 1024 bins
             uint32_t *start = (uint32_t *)sh.list;                 // keys above each bin
             unsigned long long *bkt = sh.list + 512;               // selected entries, bin by bin
+            unsigned long long *out = sh.list + 1536;              // the k chosen, in place order
             for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < kPerT; ++j)
-                if ((uint32_t)(tid + j * TK1_THREADS) < count) atomicAdd(&hist[(uint32_t)(ent[j] >> 32) - tkey], 1u);
+                if (j * TK1_THREADS < ucnt && (uint32_t)(tid + j * TK1_THREADS) < count)
+                    atomicAdd(&hist[(uint32_t)(ent[j] >> 32) - tkey], 1u);
             __syncthreads();
             uint32_t hc[4], loc = 0;
 #pragma unroll
@@ -660,9 +669,12 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             }
             __syncthreads();
             const uint32_t bk = sh.c.bcast[0];   // bin of the k-th largest key
+            uint32_t hmax = 0;   // largest bin at or above bk: one LDS atomic per wave
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if ((uint32_t)(1023 - 4 * tid - q) >= bk) atomicMax(&sh.c.bcast[1], hc[q]);
+                if ((uint32_t)(1023 - 4 * tid - q) >= bk) hmax = max(hmax, hc[q]);
+            hmax = wave_max_u32(hmax);
+            if (lane == 0 && hmax) atomicMax(&sh.c.bcast[1], hmax);
             __syncthreads();
             const uint32_t nsel = start[bk] + hist[bk], bmax = sh.c.bcast[1];
             __syncthreads();   // every thread has read nsel and bmax: the decision is uniform
@@ -672,8 +684,9 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
                 uint32_t pos[kPerT];
 #pragma unroll
                 for (int j = 0; j < kPerT; ++j) {
-                    const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey;
                     pos[j] = 0xffffffffu;
+                    if (j * TK1_THREADS >= ucnt) continue;
+                    const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey;
                     if ((uint32_t)(tid + j * TK1_THREADS) < count && dk >= bk) {
                         const uint32_t b0 = start[dk];
                         pos[j] = b0;
@@ -683,15 +696,30 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < kPerT; ++j)
-                    if (pos[j] != 0xffffffffu) {
+                    if (j * TK1_THREADS < ucnt && pos[j] != 0xffffffffu) {
                         const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey, nb = hist[dk];
                         const uint32_t myid = 0xffffffffu - (uint32_t)(ent[j] & 0xffffffffu);
-                        uint32_t rank = 0;
-                        for (uint32_t i = 0; i < nb; ++i)
-                            rank += (0xffffffffu - (uint32_t)(bkt[pos[j] + i] & 0xffffffffu)) < myid;
+                        // entries of the bin with a lower id (four reads in flight at a time)
+                        const unsigned long long *bb = bkt + pos[j];
+                        const uint32_t cmp = 0xffffffffu - myid;   // lower id <=> larger low word
+                        uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0, i = 0;
+                        for (; i + 4 <= nb; i += 4) {
+                            r0 += (uint32_t)bb[i] > cmp;
+                            r1 += (uint32_t)bb[i + 1] > cmp;
+                            r2 += (uint32_t)bb[i + 2] > cmp;
+                            r3 += (uint32_t)bb[i + 3] > cmp;
+                        }
+                        for (; i < nb; ++i) r0 += (uint32_t)bb[i] > cmp;
+                        const uint32_t rank = r0 + r1 + r2 + r3;
                         const uint32_t at = pos[j] + rank;
-                        if (at < (uint32_t)k_local) emit((int)at, tkey + dk, (int32_t)myid);
+                        if (at < (uint32_t)k_local) out[at] = ((unsigned long long)(tkey + dk) << 32) | myid;
                     }
+                __syncthreads();
+                // the k entries in place order: consecutive threads store consecutive places
+                for (int j = tid; j < k_local; j += TK1_THREADS) {
+                    const unsigned long long e = out[j];
+                    emit(j, (uint32_t)(e >> 32), (int32_t)(uint32_t)e);
+                }
                 if (tid == 0 && row_lse) row_lse[row] = lse32;
                 return;
             }
@@ -700,7 +728,7 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 #pragma unroll
             for (int j = 0; j < kPerT; ++j) {
                 const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
-                if (idx < count) sh.list[idx] = ent[j];
+                if (j * TK1_THREADS < ucnt && idx < count) sh.list[idx] = ent[j];
             }
             __syncthreads();
         }
@@ -713,14 +741,15 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 #pragma unroll
         for (int i = 0; i < TK_LIST / TK1_THREADS; ++i) {
             const uint32_t idx = (uint32_t)(tid + i * TK1_THREADS);
-            mine[i] = idx < count ? sh.list[idx] : 0ull;
+            mine[i] = i * TK1_THREADS < ucnt && idx < count ? sh.list[idx] : 0ull;
         }
         __syncthreads();
         if (tid == 0) sh.count = 0;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < TK_LIST / TK1_THREADS; ++i)
-            if ((uint32_t)(mine[i] >> 32) >= kappa) sh.list[atomicAdd(&sh.count, 1u)] = mine[i];
+            if (i * TK1_THREADS < ucnt && (uint32_t)(mine[i] >> 32) >= kappa)
+                sh.list[atomicAdd(&sh.count, 1u)] = mine[i];
         n = (int)(above + n_eq);
     } else {
         // the sample misled the threshold: cut by a radix select over the whole row
