@@ -13,8 +13,9 @@ One step = one pass of the whole hot path over synthetic inputs:
 The headline value is the prefill attention throughput in logical TFLOP/s
 (4 * D * Nq * sum L(L+1)/2 per layer, FMA = 2); decode, top-K and reorder are
 reported in algorithmic GB/s. Kernel times come from HIP events on the launching
-stream: one pair around the 28 back-to-back prefill launches of a request (the
-average launch is their span / 28) and one pair around every beam-search launch.
+stream around launches that run back to back behind a spin gate: one pair around
+the 28 prefill launches of a request (the average launch is their span / 28), and
+for decode, top-K and reorder one pair around K repeats of each step's launch.
 Inputs are drawn on the GPU from fixed seeds.
 Prints one JSON line.
 """
@@ -142,12 +143,20 @@ def main():
         del src, dst
 
     stream = torch.cuda.current_stream(dev)
-    n_ev = layers + 3 * NS
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))]
+
+    def beam_launches(s, cur):
+        """The three launches of beam-search step s (suffix length s + 1), suffix buffers suf[cur] -> suf[1 - cur]."""
+        sk, sv = suf[cur]
+        nk, nv = suf[1 - cur]
+        return (
+            lambda: bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=d_out, lse=d_lse),
+            lambda: bga.beam_topk(logits[s], cum, 2 * W, W, workspace=ws, out=topk_out),
+            lambda: bga.suffix_reorder(sk, sv, topk_out["parents"], s + 1, dst_k=nk, dst_v=nv),
+        )
 
     def step(timed):
-        """One pass of the hot path; with `timed`, HIP events bracket the prefill layers and every
-        beam-search launch."""
+        """One pass of the hot path; with `timed`, one HIP event pair brackets the prefill layers."""
         # the 28 layers run back to back, as in a request; one event pair spans them
         if timed:
             evs[0][0].record(stream)
@@ -155,26 +164,13 @@ def main():
             bga.packed_gqa_prefill(c.q, c.k, c.v, cu, max_len, out=p_out, lse=p_lse)
         if timed:
             evs[0][1].record(stream)
-        i = layers
         cur = 0
         cum.zero_()
         for s in range(NS):
-            sk, sv = suf[cur]
-            nk, nv = suf[1 - cur]
-            launches = (
-                lambda: bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=d_out, lse=d_lse),
-                lambda: bga.beam_topk(logits[s], cum, 2 * W, W, workspace=ws, out=topk_out),
-                lambda: bga.suffix_reorder(sk, sv, topk_out["parents"], s + 1, dst_k=nk, dst_v=nv),
-            )
-            for j, fn in enumerate(launches):
-                if timed:
-                    evs[i + j][0].record(stream)
+            for fn in beam_launches(s, cur):
                 fn()
-                if timed:
-                    evs[i + j][1].record(stream)
             cum.copy_(topk_out["scores"])
             cur = 1 - cur
-            i += 3
 
     for _ in range(args.warmup):
         step(True)
@@ -205,19 +201,40 @@ def main():
     gate = int(cycles_per_ms * max(3.0 * host_t * 1e3, 2.0))
 
     t_pre = 0.0
-    t_dec = [0.0] * NS
-    t_top = [0.0] * NS
-    t_reo = [0.0] * NS
     for _ in range(args.steps):
         torch.cuda._sleep(gate)
         step(True)
         torch.cuda.synchronize()   # events of this step are complete; read them
         t_pre += evs[0][0].elapsed_time(evs[0][1])
-        for s in range(NS):
-            j = layers + 3 * s
-            t_dec[s] += evs[j][0].elapsed_time(evs[j][1])
-            t_top[s] += evs[j + 1][0].elapsed_time(evs[j + 1][1])
-            t_reo[s] += evs[j + 2][0].elapsed_time(evs[j + 2][1])
+
+    # Beam-search kernels, each timed by itself: K launches back to back behind the gate with one event
+    # pair around them (an event pair around one short launch would also count its dispatch gap), the
+    # launches rotating over input sets that together exceed the 256 MB Infinity Cache (four decode
+    # sets of 160 MB; the five 194 MB logits tensors). Average launch = span / K.
+    dsets = [dc] + [wl.make_decode_case(R, W, LP, NS, NQ, NKV, D, bcfg["seed"] * 1000 + i, dev) for i in range(1, 4)]
+    torch.cuda.synchronize()
+
+    def back_to_back(fns):
+        fns[0]()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(gate)
+        evs[0][0].record(stream)
+        for i in range(args.steps):
+            fns[i % len(fns)]()
+        evs[0][1].record(stream)
+        torch.cuda.synchronize()
+        return evs[0][0].elapsed_time(evs[0][1])
+
+    t_dec, t_reo = [0.0] * NS, [0.0] * NS
+    for s in range(NS):
+        t_dec[s] = back_to_back([lambda ds=ds, s=s: bga.shared_prefix_decode(ds.q, ds.prefix_k, ds.prefix_v, ds.suffix_k,
+                                                                              ds.suffix_v, s + 1, out=d_out, lse=d_lse)
+                                 for ds in dsets])
+        t_reo[s] = back_to_back([lambda ds=ds, s=s: bga.suffix_reorder(ds.suffix_k, ds.suffix_v, topk_out["parents"],
+                                                                        s + 1, dst_k=suf[1][0], dst_v=suf[1][1])
+                                 for ds in dsets])
+    t_top = [back_to_back([lambda j=j: bga.beam_topk(logits[j], cum, 2 * W, W, workspace=ws, out=topk_out)
+                           for j in range(NS)])] * NS
 
     K = args.steps
     pre_flops = wl.prefill_flops(lengths, pcfg["nq"], pcfg["d"])
