@@ -46,10 +46,10 @@ KERNEL_SOURCES = {
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
 MEASURED_TRAFFIC = {
-    "packed_gqa_prefill": {"fetch_kib": 17173.7, "write_kib": 17972.2, "sources_sha256": "63a7f5e4487d387a"},
-    "shared_prefix_decode": {"fetch_kib": 34130.7, "write_kib": 14944.0, "sources_sha256": "35756fe22eeed70b"},
-    "beam_topk": {"fetch_kib": 486908.0, "write_kib": 20418.7, "sources_sha256": "e3c0a399665c05a1"},
-    "suffix_reorder": {"fetch_kib": 15192.4, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
+    "packed_gqa_prefill": {"fetch_kib": 17173.9, "write_kib": 17972.2, "sources_sha256": "63a7f5e4487d387a"},
+    "shared_prefix_decode": {"fetch_kib": 34130.2, "write_kib": 14944.1, "sources_sha256": "35756fe22eeed70b"},
+    "beam_topk": {"fetch_kib": 487023.4, "write_kib": 20037.5, "sources_sha256": "387ba3c5334eb011"},
+    "suffix_reorder": {"fetch_kib": 14882.8, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
 }
 
 
