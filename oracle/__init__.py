@@ -20,26 +20,29 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the loader at another build of the same source (the
+# mutation check of the pins does, with a planted mistake).
+_LIB_OVERRIDE = os.environ.get("BGA_ORACLE_LIB")
 _lib = None
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into liboracle.so next to it."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-               "-std=c11", _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile oracle.c (or `src`) with gcc into liboracle.so next to it (or `out`)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        subprocess.run(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = _LIB_OVERRIDE or _LIB
+        if not _LIB_OVERRIDE and not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, f64 = ctypes.c_int32, ctypes.c_double
         L.oracle_packed_prefill.argtypes = [P, P, P, P, i32, i32, i32, i32, f64, P, P, i32]

@@ -150,9 +150,11 @@ def small_decode(r=2, w=5, lp=7, ls_cap=3, nq=4, nkv=2, d=64, seed=21):
     return wl.make_decode_case(r, w, lp, ls_cap, nq, nkv, d, seed)
 
 
-@pytest.mark.parametrize("ls", [0, 1, 3])
-def test_decode_matches_sdpa_over_concat(ls):
-    c = small_decode()
+@pytest.mark.parametrize("ls,w", [(0, 5), (1, 5), (3, 5), (2, 1)])
+def test_decode_matches_sdpa_over_concat(ls, w):
+    """SDPA (float64) over the explicit [prompt; suffix] of every beam; W = 1 is
+    ordinary single-sequence decode."""
+    c = small_decode(w=w)
     scale = 1.0 / np.sqrt(c.d)
     o, lse = oracle.shared_prefix_decode(c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, ls, scale)
     g = c.nq // c.nkv
