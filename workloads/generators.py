@@ -24,8 +24,11 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-# Named workloads. Sizes follow the stated workload shapes; see the design doc for
-# the mapping to the article's own (unpublished-size) workloads.
+# Named workloads: synthetic stand-ins with the shapes of the article's
+# scenarios (its own business traffic and datasets are not public): a
+# Prefill-Only request (15 sequences of 64..480 tokens, 28 layers), long
+# packed prefill (lognormal lengths around 400, or 120 x 1024), short-prompt
+# and long-prompt beam search.
 CONFIGS = {
     "tiny_prefill": dict(kind="prefill", lengths=[5, 17, 40], nq=4, nkv=2, d=64, seed=0),
     "prefill_only": dict(kind="prefill", dist="uniform", n=15, lo=64, hi=480,
