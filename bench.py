@@ -102,6 +102,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calib_copy_mb > 0:   # one plain device copy of known size, for counter calibration
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.only:
         print(json.dumps(only_config(args, dev)), flush=True)
         return
@@ -133,14 +140,6 @@ def main():
                 "scores": torch.empty((R, W), dtype=torch.float32, device=dev)}
     cum = torch.zeros((R, W), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-
-    if args.calib_copy_mb > 0:
-        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     stream = torch.cuda.current_stream(dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))]
