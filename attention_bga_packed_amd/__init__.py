@@ -8,11 +8,14 @@ fallback path.
 """
 from ._binding import (  # noqa: F401
     BgaError,
+    DEBUG_LIB_PATH,
     EXPORTS,
     LIB_PATH,
+    RELEASE_LIB_PATH,
     beam_topk,
     beam_topk_workspace_size,
     lib,
+    load_library,
     packed_gqa_prefill,
     shared_prefix_decode,
     suffix_reorder,

@@ -1,9 +1,14 @@
 """Thin ctypes binding of libbga.so (argument marshalling only).
 
-Every call checks tensor dtypes/devices/shapes, allocates missing outputs with
-torch on the input's device, and forwards raw device pointers plus the current
-torch stream to the C-ABI. All arithmetic happens in the HIP kernels; if the
-library is missing, importing this module raises.
+Every call checks tensor dtypes, devices, contiguity and exact shapes (inputs
+and caller-provided outputs alike), allocates missing outputs with torch on the
+input's device, and forwards raw device pointers plus the current torch stream
+to the C-ABI. All arithmetic happens in the HIP kernels; if the library is
+missing, importing this module raises.
+
+The library loaded is attention_bga_packed_amd/libbga.so, or the file named by
+the environment variable BGA_LIBRARY (for instance libbga_debug.so, the build
+that checks device-side preconditions).
 """
 from __future__ import annotations
 
@@ -14,15 +19,18 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbga.so")
+RELEASE_LIB_PATH = os.path.join(_HERE, "libbga.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libbga_debug.so")
+LIB_PATH = os.environ.get("BGA_LIBRARY") or RELEASE_LIB_PATH
 
 STATUS_NAMES = {0: "BGA_OK", 1: "BGA_ERR_NULL", 2: "BGA_ERR_SHAPE", 3: "BGA_ERR_UNSUPPORTED",
-                4: "BGA_ERR_ALIGN", 5: "BGA_ERR_WORKSPACE", 6: "BGA_ERR_ALIAS", 7: "BGA_ERR_HIP"}
+                4: "BGA_ERR_ALIGN", 5: "BGA_ERR_WORKSPACE", 6: "BGA_ERR_ALIAS", 7: "BGA_ERR_HIP",
+                8: "BGA_ERR_PRECONDITION"}
 
 # Every symbol declared in include/bga.h.
 EXPORTS = ("bga_packed_gqa_prefill", "bga_shared_prefix_decode", "bga_suffix_reorder",
            "bga_beam_topk_workspace_size", "bga_beam_topk", "bga_status_string", "bga_last_hip_error",
-           "bga_version")
+           "bga_version", "bga_debug_build", "bga_last_violations")
 
 
 class BgaError(RuntimeError):
@@ -31,10 +39,11 @@ class BgaError(RuntimeError):
         super().__init__(f"{where}: {detail or STATUS_NAMES.get(status, status)}")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_bga_packed_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+def load_library(path: str = LIB_PATH):
+    """ctypes handle of a libbga build with every entry point's signature set."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m attention_bga_packed_amd.build`")
+    L = ctypes.CDLL(path)
     P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     L.bga_packed_gqa_prefill.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, P, P, P]
     L.bga_shared_prefix_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P, P]
@@ -46,13 +55,16 @@ def _load():
     L.bga_status_string.restype = ctypes.c_char_p
     L.bga_last_hip_error.argtypes = []
     L.bga_version.argtypes = []
+    L.bga_debug_build.argtypes = []
+    L.bga_last_violations.argtypes = []
+    L.bga_last_violations.restype = ctypes.c_uint32
     for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_suffix_reorder, L.bga_beam_topk,
-              L.bga_last_hip_error, L.bga_version):
+              L.bga_last_hip_error, L.bga_version, L.bga_debug_build):
         f.restype = i32
     return L
 
 
-lib = _load()
+lib = load_library()
 
 
 def _check(status: int, where: str):
@@ -60,6 +72,8 @@ def _check(status: int, where: str):
         detail = lib.bga_status_string(status).decode()
         if status == 7:
             detail += f" (hipError {lib.bga_last_hip_error()})"
+        if status == 8:
+            detail += f" (violations 0x{lib.bga_last_violations():x})"
         raise BgaError(status, where, detail)
 
 
@@ -71,7 +85,7 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _need(t, name, dtype, device=None, ndim=None):
+def _need(t, name, dtype, device=None, ndim=None, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -82,6 +96,8 @@ def _need(t, name, dtype, device=None, ndim=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -103,11 +119,11 @@ def packed_gqa_prefill(q, k, v, cu_seqlens, max_seqlen: int, softmax_scale=None,
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", torch.bfloat16, dev)
+    _need(out, "out", torch.bfloat16, dev, shape=q.shape)
     if lse is None and want_lse:
         lse = torch.empty((t, nq), dtype=torch.float32, device=dev)
     if lse is not None:
-        _need(lse, "lse", torch.float32, dev)
+        _need(lse, "lse", torch.float32, dev, shape=(t, nq))
     st = lib.bga_packed_gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, t,
                                     int(max_seqlen), nq, nkv, d, float(softmax_scale), _ptr(out), _ptr(lse),
                                     _stream(q))
@@ -136,11 +152,11 @@ def shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, suffix_len: 
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", torch.bfloat16, dev)
+    _need(out, "out", torch.bfloat16, dev, shape=q.shape)
     if lse is None and want_lse:
         lse = torch.empty((r, w, nq), dtype=torch.float32, device=dev)
     if lse is not None:
-        _need(lse, "lse", torch.float32, dev)
+        _need(lse, "lse", torch.float32, dev, shape=(r, w, nq))
     st = lib.bga_shared_prefix_decode(_ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(suffix_k), _ptr(suffix_v), r, w,
                                       lp, int(suffix_len), ls_cap, nq, nkv, d, float(softmax_scale), _ptr(out),
                                       _ptr(lse), _stream(q))
@@ -154,22 +170,26 @@ def suffix_reorder(src_k, src_v, parent, suffix_len: int, dst_k=None, dst_v=None
     src/dst [R,W,Ls_cap,Nkv,D] bf16; parent [R,W] int32; tokens [R,W,tok_cap] int32."""
     _need(src_k, "src_k", torch.bfloat16, ndim=5)
     dev = src_k.device
-    _need(src_v, "src_v", torch.bfloat16, dev, 5)
-    _need(parent, "parent", torch.int32, dev, 2)
     r, w, ls_cap, nkv, d = src_k.shape
+    _need(src_v, "src_v", torch.bfloat16, dev, shape=src_k.shape)
+    _need(parent, "parent", torch.int32, dev, shape=(r, w))
     if dst_k is None:
         dst_k = torch.empty_like(src_k)
     if dst_v is None:
         dst_v = torch.empty_like(src_v)
-    _need(dst_k, "dst_k", torch.bfloat16, dev, 5)
-    _need(dst_v, "dst_v", torch.bfloat16, dev, 5)
+    _need(dst_k, "dst_k", torch.bfloat16, dev, shape=src_k.shape)
+    _need(dst_v, "dst_v", torch.bfloat16, dev, shape=src_k.shape)
     tok_cap = 0
+    if src_tokens is None and dst_tokens is not None:
+        raise ValueError("dst_tokens given without src_tokens")
     if src_tokens is not None:
         _need(src_tokens, "src_tokens", torch.int32, dev, 3)
+        if src_tokens.shape[:2] != (r, w):
+            raise ValueError(f"src_tokens must be [R, W, tok_cap] with R, W = {r}, {w}")
         tok_cap = src_tokens.shape[2]
         if dst_tokens is None:
             dst_tokens = torch.empty_like(src_tokens)
-        _need(dst_tokens, "dst_tokens", torch.int32, dev, 3)
+        _need(dst_tokens, "dst_tokens", torch.int32, dev, shape=src_tokens.shape)
     st = lib.bga_suffix_reorder(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(parent), _ptr(src_tokens),
                                 _ptr(dst_tokens), r, w, int(suffix_len), ls_cap, nkv, d, int(num_tokens), tok_cap,
                                 _stream(src_k))
@@ -189,20 +209,26 @@ def beam_topk(logits, cum_scores, k_local: int, k_global: int, workspace=None, w
     dev = logits.device
     r, w_in, vocab = logits.shape
     if cum_scores is not None:
-        _need(cum_scores, "cum_scores", torch.float32, dev, 2)
+        _need(cum_scores, "cum_scores", torch.float32, dev, shape=(r, w_in))
     need = beam_topk_workspace_size(r, w_in, vocab, k_local, k_global)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, dev)
+    _need(workspace, "workspace", torch.uint8, dev, 1)
     res = out if out is not None else {}
-    res.setdefault("tokens", torch.empty((r, k_global), dtype=torch.int32, device=dev))
-    res.setdefault("parents", torch.empty((r, k_global), dtype=torch.int32, device=dev))
-    res.setdefault("scores", torch.empty((r, k_global), dtype=torch.float32, device=dev))
-    if want_local:
-        res.setdefault("local_tokens", torch.empty((r, w_in, k_local), dtype=torch.int32, device=dev))
-        res.setdefault("local_scores", torch.empty((r, w_in, k_local), dtype=torch.float32, device=dev))
-    if want_lse:
-        res.setdefault("row_lse", torch.empty((r, w_in), dtype=torch.float32, device=dev))
+    shapes = {"tokens": ((r, k_global), torch.int32), "parents": ((r, k_global), torch.int32),
+              "scores": ((r, k_global), torch.float32)}
+    if want_local or "local_tokens" in res or "local_scores" in res:
+        shapes["local_tokens"] = ((r, w_in, k_local), torch.int32)
+        shapes["local_scores"] = ((r, w_in, k_local), torch.float32)
+    if want_lse or "row_lse" in res:
+        shapes["row_lse"] = ((r, w_in), torch.float32)
+    unknown = set(res) - set(shapes)
+    if unknown:
+        raise ValueError(f"unknown beam_topk outputs {sorted(unknown)}")
+    for key, (shape, dtype) in shapes.items():
+        if key not in res:
+            res[key] = torch.empty(shape, dtype=dtype, device=dev)
+        _need(res[key], key, dtype, dev, shape=shape)
     st = lib.bga_beam_topk(_ptr(logits), _ptr(cum_scores), r, w_in, vocab, int(k_local), int(k_global),
                            _ptr(res["tokens"]), _ptr(res["parents"]), _ptr(res["scores"]),
                            _ptr(res.get("local_tokens")), _ptr(res.get("local_scores")), _ptr(res.get("row_lse")),

@@ -3,7 +3,9 @@
     python -m attention_bga_packed_amd.build
 
 Each csrc/*.hip is compiled with hipcc in parallel into _build/, then linked
-into attention_bga_packed_amd/libbga.so.
+into attention_bga_packed_amd/libbga.so. The debug library libbga_debug.so is
+linked from the same kernel objects plus the C-ABI layer and the device-side
+precondition checks compiled with -DBGA_DEBUG.
 """
 from __future__ import annotations
 
@@ -16,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbga.so")
+DEBUG_LIB = os.path.join(PKG, "libbga_debug.so")
+# sources compiled a second time, with -DBGA_DEBUG, for the debug library
+DEBUG_SOURCES = ("bga_abi.hip", "debug_checks.hip")
 ARCH = os.environ.get("BGA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -37,14 +42,11 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    hipcc = os.environ.get("HIPCC", "hipcc")
-    procs, objs = [], []
-    for src in sources():
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-        objs.append(obj)
-        cmd = [hipcc, *HIPCC_FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile_all(jobs, hipcc, verbose):
+    """jobs: [(src, obj, extra flags)], compiled in parallel; raises on any failure."""
+    procs = []
+    for src, obj, extra in jobs:
+        cmd = [hipcc, *HIPCC_FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -60,9 +62,33 @@ def build(verbose: bool = False) -> str:
         for src, out in failed:
             print(f"--- {src}\n{out}", file=sys.stderr)
         raise RuntimeError("hipcc failed for " + ", ".join(os.path.basename(s) for s, _ in failed))
-    tmp = LIB + ".tmp"
+
+
+def _link(hipcc, objs, lib):
+    tmp = lib + ".tmp"
     subprocess.run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    debug_dir = os.path.join(BUILD, "debug")
+    os.makedirs(debug_dir, exist_ok=True)
+    hipcc = os.environ.get("HIPCC", "hipcc")
+    jobs, objs, debug_objs = [], [], []
+    for src in sources():
+        base = os.path.basename(src)[:-4] + ".o"
+        obj = os.path.join(BUILD, base)
+        jobs.append((src, obj, []))
+        objs.append(obj)
+        if os.path.basename(src) in DEBUG_SOURCES:
+            dobj = os.path.join(debug_dir, base)
+            jobs.append((src, dobj, ["-DBGA_DEBUG"]))
+            debug_objs.append(dobj)
+        else:
+            debug_objs.append(obj)
+    _compile_all(jobs, hipcc, verbose)
+    _link(hipcc, objs, LIB)
+    _link(hipcc, debug_objs, DEBUG_LIB)
     return LIB
 
 

@@ -37,6 +37,14 @@
 // probability; until then probabilities up to 256 are accumulated, which fp32
 // and bf16 represent as well as values up to 1. The result is the same softmax
 // (numerator and denominator use the same reference).
+//
+// Two row sums are kept. The P*V product sees every probability rounded to
+// bf16, so O is normalised by the sum of those same rounded values (ln, one
+// v_dot2 per pair): the output is then an exact convex combination of the V
+// rows with weights off by the rounding only, which keeps it within 1e-2 of
+// the exact softmax for outputs up to 4 in magnitude (a numerator of rounded
+// and a denominator of unrounded probabilities can miss by 0.0105 there). The
+// log-sum-exp uses the sum of the fp32 probabilities (l).
 #pragma once
 
 #include <type_traits>
@@ -232,9 +240,10 @@ struct Wave {
     f32x16 o[D / 32];   // O^T: lane holds row (lane & 31), d = b*32 + (r/4)*8 + (lane>>5)*4 + r%4
     float m;            // reference maximum of the raw scores q.k (unscaled)
     float mc;           // m * c2
-    float l;            // partial row sum over the keys this lane holds
+    float l;            // partial row sum of the fp32 probabilities of the keys this lane holds
+    float ln;           // the same over the bf16-rounded probabilities (normalises O)
     uint32_t pk[2][8];  // bf16 P^T of the current tile: pk[kb][j] = keys of elements 2j, 2j+1
-    float psum;
+    float psum, psn;
 
     // empty state: no keys seen
     __device__ __forceinline__ void reset()
@@ -244,6 +253,7 @@ struct Wave {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
         l = 0.f;
+        ln = 0.f;
         m = -INFINITY;
         mc = -INFINITY;
     }
@@ -254,10 +264,15 @@ struct Wave {
         const int kb = p >> 3, r = (p & 7) * 2;
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -mc));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c2, -mc));
-        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+        const uint32_t packed = pack_bf16x2(p0, p1);
+        pk[kb][r >> 1] = packed;
         // fp32 probabilities: the log-sum-exp keeps full precision
         psum = p == 0 ? p0 + p1 : psum + (p0 + p1);
         keep(psum);
+        // the rounded probabilities the P*V product sees
+        psn = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                              __builtin_bit_cast(bf16x2, 0x3f803f80u), p == 0 ? 0.f : psn, false);
+        keep(psn);
     }
 
     // one P*V MFMA: d block b, keys kb*32 + kk*16 + [0, 16), V^T operand va
@@ -300,6 +315,7 @@ struct Wave {
             m = m_new;
             mc = m_new * c2;
             l *= alpha;
+            ln *= alpha;
 #pragma unroll
             for (int b = 0; b < D / 32; ++b)
 #pragma unroll
@@ -371,7 +387,10 @@ struct Wave {
 #pragma unroll
                 for (int p = E1 + i * 2 * (16 - E1) / NPV; p < E1 + (i + 1) * 2 * (16 - E1) / NPV; ++p)
                     exp_pair(sc, p, c2);
-                if (i == NPV / 2 - 1) l += psum;
+                if (i == NPV / 2 - 1) {
+                    l += psum;
+                    ln += psn;
+                }
             } else if (i == NPV / 2) {
                 mx = rowmax(sn);
             }
@@ -406,6 +425,7 @@ struct Wave {
             fence();
         }
         l += psum;
+        ln += psn;
     }
 
     // Final normalisation and stores of the wave's 32 rows. This lane's row is
@@ -425,7 +445,7 @@ struct Wave {
         constexpr int RPI = 64 / CH;    // rows per store instruction
         const int lane = lane_id(), col = lane & 31, half = lane >> 5;
         const float lt = pair_sum(l);
-        const float inv = 1.f / lt;
+        const float inv = 1.f / pair_sum(ln);
 #pragma unroll
         for (int b = 0; b < D / 32; ++b)
 #pragma unroll

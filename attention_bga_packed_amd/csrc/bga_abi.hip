@@ -10,6 +10,7 @@
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
+thread_local uint32_t g_last_violations = 0;
 
 bga_status hip_status(hipError_t e)
 {
@@ -17,6 +18,19 @@ bga_status hip_status(hipError_t e)
     g_last_hip_error = (int32_t)e;
     return BGA_ERR_HIP;
 }
+
+#ifdef BGA_DEBUG
+// Outcome of a debug build's device-side check: a HIP error, a violation, or go.
+bga_status check_status(hipError_t e, uint32_t violations)
+{
+    if (e != hipSuccess) return hip_status(e);
+    if (violations) {
+        g_last_violations = violations;
+        return BGA_ERR_PRECONDITION;
+    }
+    return BGA_OK;
+}
+#endif
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -49,8 +63,9 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
     if (num_seqs > 65535 || max_seqlen > BGA_MAX_SEQLEN) return BGA_ERR_UNSUPPORTED;
     if ((int64_t)total_tokens * num_q_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // output row index
     if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
+    if (total_tokens > 0 && (num_seqs == 0 || max_seqlen == 0)) return BGA_ERR_SHAPE;   // rows nobody would write
     if (!cu_seqlens) return BGA_ERR_NULL;
-    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return BGA_OK;
+    if (total_tokens == 0) return BGA_OK;
     if (!q || !k || !v || !out) return BGA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(cu_seqlens, 4) ||
         (lse && !aligned(lse, 4)))
@@ -59,6 +74,14 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
     const size_t kvbytes = (size_t)total_tokens * num_kv_heads * head_dim * 2;
     if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kvbytes) || overlap(out, qbytes, v, kvbytes))
         return BGA_ERR_ALIAS;
+#ifdef BGA_DEBUG
+    {
+        uint32_t bad = 0;
+        const bga_status st =
+            check_status(bga::debug_check_prefill(cu_seqlens, num_seqs, total_tokens, max_seqlen, stream, &bad), bad);
+        if (st != BGA_OK) return st;
+    }
+#endif
     return hip_status(bga::launch_packed_prefill(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_q_heads,
                                                  num_kv_heads, head_dim, softmax_scale, out, lse, stream));
 }
@@ -112,6 +135,7 @@ bga_status bga_suffix_reorder(const bga_bf16 *src_k, const bga_bf16 *src_v, bga_
     if (num_kv_heads <= 0) return BGA_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
     if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * beam_width > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // one workgroup per beam
     if ((src_tokens == nullptr) != (dst_tokens == nullptr)) return BGA_ERR_NULL;
     if (src_tokens && (num_tokens < 0 || tok_cap < 0 || num_tokens > tok_cap)) return BGA_ERR_SHAPE;
     if (num_requests == 0 || beam_width == 0) return BGA_OK;
@@ -127,6 +151,14 @@ bga_status bga_suffix_reorder(const bga_bf16 *src_k, const bga_bf16 *src_v, bga_
         const size_t tb = (size_t)num_requests * beam_width * tok_cap * 4;
         if (overlap(dst_tokens, tb, src_tokens, tb)) return BGA_ERR_ALIAS;
     }
+#ifdef BGA_DEBUG
+    {
+        uint32_t bad = 0;
+        const bga_status st =
+            check_status(bga::debug_check_parents(parent, num_requests * beam_width, beam_width, stream, &bad), bad);
+        if (st != BGA_OK) return st;
+    }
+#endif
     return hip_status(bga::launch_suffix_reorder(src_k, src_v, dst_k, dst_v, parent, src_tokens, dst_tokens,
                                                  num_requests, beam_width, suffix_len, suffix_cap, num_kv_heads,
                                                  head_dim, src_tokens ? num_tokens : 0, tok_cap, stream));
@@ -138,6 +170,7 @@ static bool topk_sizes_ok(int32_t R, int32_t W_in, int32_t V, int32_t k_local, i
     if (W_in > BGA_MAX_BEAMS || V > BGA_MAX_VOCAB || k_local > V || k_local > BGA_MAX_K || k_global > BGA_MAX_K)
         return false;
     if ((int64_t)k_global > (int64_t)W_in * k_local) return false;
+    if ((int64_t)R * W_in > 0x7fffffff) return false;   // one workgroup per beam row
     return true;
 }
 
@@ -169,6 +202,13 @@ bga_status bga_beam_topk(const bga_bf16 *logits, const float *cum_scores, int32_
         return BGA_ERR_ALIGN;
     const size_t lbytes = (size_t)num_requests * num_src_beams * vocab * 2;
     if (overlap(workspace, need, logits, lbytes)) return BGA_ERR_ALIAS;
+#ifdef BGA_DEBUG
+    {
+        uint32_t bad = 0;
+        const bga_status st = check_status(bga::debug_check_logits(logits, lbytes / 2, stream, &bad), bad);
+        if (st != BGA_OK) return st;
+    }
+#endif
     return hip_status(bga::launch_beam_topk(logits, cum_scores, num_requests, num_src_beams, vocab, k_local,
                                             k_global, out_tokens, out_parents, out_scores, local_tokens,
                                             local_scores, row_lse, workspace, stream));
@@ -185,12 +225,24 @@ const char *bga_status_string(bga_status s)
     case BGA_ERR_WORKSPACE: return "BGA_ERR_WORKSPACE: workspace missing or too small";
     case BGA_ERR_ALIAS: return "BGA_ERR_ALIAS: an output overlaps an input";
     case BGA_ERR_HIP: return "BGA_ERR_HIP: a HIP launch failed";
+    case BGA_ERR_PRECONDITION: return "BGA_ERR_PRECONDITION: a device-side precondition does not hold (debug build)";
     }
     return "unknown bga_status";
 }
 
 int32_t bga_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t bga_version(void) { return 100; }
+int32_t bga_version(void) { return 200; }
+
+int32_t bga_debug_build(void)
+{
+#ifdef BGA_DEBUG
+    return 1;
+#else
+    return 0;
+#endif
+}
+
+uint32_t bga_last_violations(void) { return g_last_violations; }
 
 }  // extern "C"

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
             const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * c2);   // 0 while no key was seen (m = -inf)
             const float p = __builtin_amdgcn_exp2f((s - m_new) * c2);
             st.l = st.l * alpha + (half == 0 ? p : 0.f);
+            st.ln = st.ln * alpha + (half == 0 ? p : 0.f);   // the suffix weights p exactly (fp32)
             st.m = m_new;
 #pragma unroll
             for (int b = 0; b < D / 32; ++b)

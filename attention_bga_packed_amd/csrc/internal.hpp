@@ -36,4 +36,14 @@ hipError_t launch_beam_topk(const uint16_t *logits, const float *cum, int R, int
                             int32_t *local_tok, float *local_score, float *row_lse, void *workspace,
                             hipStream_t stream);
 
+#ifdef BGA_DEBUG
+// Debug build: device-side precondition checks (debug_checks.hip). Each runs a
+// check kernel on `stream`, waits for it and returns the BGA_VIOLATION_* bits
+// found in *violations.
+hipError_t debug_check_prefill(const int32_t *cu, int B, int T, int max_seqlen, hipStream_t stream,
+                               uint32_t *violations);
+hipError_t debug_check_parents(const int32_t *parent, int n, int W, hipStream_t stream, uint32_t *violations);
+hipError_t debug_check_logits(const uint16_t *x, size_t n, hipStream_t stream, uint32_t *violations);
+#endif
+
 }  // namespace bga

@@ -469,7 +469,8 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             hm |= (bf16_lo(d[e]) >= tval ? 1u : 0u) << (2 * e);
             hm |= (bf16_hi(d[e]) >= tval ? 1u : 0u) << (2 * e + 1);
         }
-        // finite logits: value order is key order; ids >= V are padding
+        // finite logits: value order is key order. Only chunks inside the row
+        // are queued (c < nchunks, so 1 <= V - 8c); its ids >= V are padding.
         hm = have ? hm & ((1u << min(8, V - c * 8)) - 1u) : 0u;
         const uint32_t cnt = (uint32_t)__popc(hm);
         const uint32_t incl = wave_incl_scan_u32(cnt);
@@ -529,8 +530,8 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             acc += (double)cs;
         }
 #pragma unroll
-        for (int u = 0; u < TK1_UNROLL; ++u) {   // queue the chunks that hold keys >= t
-            const bool hit = cmax[u] >= tval;
+        for (int u = 0; u < TK1_UNROLL; ++u) {   // queue the row's chunks that hold keys >= t
+            const bool hit = cmax[u] >= tval && (i0 + u) * TK1_THREADS + tid < nchunks;
             const unsigned long long mask = __ballot(hit);
             if (mask) {   // wave-uniform; the wave's own ring, no atomics
                 const uint32_t pos = rpos + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

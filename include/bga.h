@@ -22,7 +22,12 @@
  *     BEFORE any device call: nothing is enqueued. BGA_ERR_HIP reports a failed
  *     launch; bga_last_hip_error() then returns the hipError_t.
  *   - Preconditions on device data (valid cu_seqlens, parent indices in range,
- *     finite logits) are documented per call and not checked.
+ *     finite logits) are documented per call. The release library does not
+ *     check them. The debug library (libbga_debug.so, built with BGA_DEBUG)
+ *     checks them on the device before each operation: it waits for the check
+ *     on `stream` (the only calls that synchronize) and, when one fails,
+ *     returns BGA_ERR_PRECONDITION without launching the operation, with the
+ *     failed checks in bga_last_violations().
  *   - Calls on different streams may run concurrently; the library is reentrant.
  */
 #ifndef BGA_H
@@ -47,15 +52,24 @@ typedef enum {
     BGA_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
     BGA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     BGA_ERR_ALIAS = 6,       /* output overlaps an input that must stay intact */
-    BGA_ERR_HIP = 7          /* a HIP launch failed; see bga_last_hip_error() */
+    BGA_ERR_HIP = 7,         /* a HIP launch failed; see bga_last_hip_error() */
+    BGA_ERR_PRECONDITION = 8 /* debug build only: a device-side precondition does not hold;
+                                see bga_last_violations(); nothing was computed */
 } bga_status;
 
+/* Bits of bga_last_violations(): the device-side preconditions a debug build checks. */
+#define BGA_VIOLATION_CU_SEQLENS 1u  /* cu_seqlens[0] != 0, decreasing, or cu_seqlens[B] != total_tokens */
+#define BGA_VIOLATION_MAX_SEQLEN 2u  /* a sequence is longer than max_seqlen */
+#define BGA_VIOLATION_PARENT 4u      /* a parent index outside [0, W) */
+#define BGA_VIOLATION_LOGITS 8u      /* a logit is inf or NaN */
+
 /* Caps (the article bounds its workloads to <= 400 beams, <= 5 generated
- * tokens and prompts averaging under 500 tokens, section 1.2). */
+ * tokens and prompts averaging under 500 tokens, section 1.2). Each cap is
+ * exercised on the GPU by the parity tests. */
 #define BGA_MAX_GROUP 16        /* num_q_heads / num_kv_heads */
-#define BGA_MAX_SEQLEN 65536    /* longest packed sequence */
-#define BGA_MAX_BEAMS 1024      /* beam_width / num_src_beams */
-#define BGA_MAX_SUFFIX 64       /* suffix_cap */
+#define BGA_MAX_SEQLEN 8192     /* longest packed sequence; longest prompt */
+#define BGA_MAX_BEAMS 512       /* beam_width / num_src_beams */
+#define BGA_MAX_SUFFIX 16       /* suffix_cap */
 #define BGA_MAX_K 1024          /* k_local and k_global */
 #define BGA_MAX_VOCAB 163840    /* vocabulary size */
 
@@ -70,7 +84,8 @@ typedef enum {
  *            total_tokens = T. Sequence i owns rows cu[i] .. cu[i+1]-1. Zero-length
  *            sequences are allowed.
  *   max_seqlen >= every cu[i+1]-cu[i] (precondition; rows of a longer sequence
- *            beyond max_seqlen are not written).
+ *            beyond max_seqlen are not written), <= BGA_MAX_SEQLEN, and >= 1
+ *            when total_tokens > 0 (else BGA_ERR_SHAPE).
  *   Query head h reads K/V head h / (num_q_heads / num_kv_heads).
  *   A query at position t of its sequence attends to positions 0..t of the
  *   same sequence; scores are softmax_scale * <q, k>.
@@ -177,6 +192,12 @@ int32_t bga_last_hip_error(void);
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int32_t bga_version(void);
+
+/* 1 in the debug library (device-side precondition checks), 0 in the release library. */
+int32_t bga_debug_build(void);
+
+/* BGA_VIOLATION_* bits of the most recent BGA_ERR_PRECONDITION on the calling thread (0 if none). */
+uint32_t bga_last_violations(void);
 
 #ifdef __cplusplus
 }

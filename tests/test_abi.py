@@ -30,11 +30,33 @@ def test_exports_match_header(m):
 
 
 def test_status_strings(m):
-    for code in range(8):
+    for code in range(9):
         s = m.lib.bga_status_string(code).decode()
         assert s.startswith("BGA_")
+        assert s.split(":")[0] == m._binding.STATUS_NAMES[code]
     assert m.lib.bga_last_hip_error() == 0
-    assert m.lib.bga_version() >= 100
+    assert m.lib.bga_last_violations() == 0
+    assert m.lib.bga_version() >= 200
+
+
+def test_release_and_debug_builds():
+    from attention_bga_packed_amd import _binding
+    rel = _binding.load_library(_binding.RELEASE_LIB_PATH)
+    dbg = _binding.load_library(_binding.DEBUG_LIB_PATH)
+    assert rel.bga_debug_build() == 0 and dbg.bga_debug_build() == 1
+    for s in header_symbols():
+        assert hasattr(dbg, s), s
+
+
+def header_caps():
+    text = open(os.path.join(ROOT, "include", "bga.h")).read()
+    return {k: int(v) for k, v in re.findall(r"#define (BGA_MAX_[A-Z]+) (\d+)", text)}
+
+
+def test_caps_are_the_contract():
+    # the article's bounds with headroom: <= 512 beams, <= 16 suffix tokens, sequences <= 8192 tokens
+    assert header_caps() == {"BGA_MAX_GROUP": 16, "BGA_MAX_SEQLEN": 8192, "BGA_MAX_BEAMS": 512,
+                             "BGA_MAX_SUFFIX": 16, "BGA_MAX_K": 1024, "BGA_MAX_VOCAB": 163840}
 
 
 P = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced on these paths
@@ -58,8 +80,11 @@ def test_prefill_errors(m):
     assert prefill(m, lse=6 * P + 2) == 4
     assert prefill(m, out=P) == 6                 # out aliases q
     assert prefill(m, maxL=1 << 20) == 3
+    assert prefill(m, maxL=8193) == 3
+    assert prefill(m, maxL=0) == 2                # rows exist but no sequence may hold one
+    assert prefill(m, B=0) == 2
     assert prefill(m, T=0) == 0                   # nothing to do, nothing launched
-    assert prefill(m, B=0) == 0
+    assert prefill(m, T=0, B=0, maxL=0) == 0
 
 
 def decode(m, q=P, pk=2 * P, pv=3 * P, sk=4 * P, sv=5 * P, R=2, W=4, Lp=8, Ls=2, cap=3, nq=4, nkv=2, d=64,
@@ -71,7 +96,10 @@ def test_decode_errors(m):
     assert decode(m, Ls=4, cap=3) == 2
     assert decode(m, Lp=0, Ls=0) == 2
     assert decode(m, W=2000) == 3
+    assert decode(m, W=513) == 3
     assert decode(m, cap=100, Ls=1) == 3
+    assert decode(m, cap=17, Ls=1) == 3
+    assert decode(m, Lp=8193) == 3
     assert decode(m, d=80) == 3
     assert decode(m, sk=None) == 1
     assert decode(m, pk=None) == 1
@@ -92,6 +120,8 @@ def test_reorder_errors(m):
     assert reorder(m, dk=P) == 6                  # dst overlaps src
     assert reorder(m, par=None) == 1
     assert reorder(m, dk=3 * P + 2) == 4
+    assert reorder(m, W=513) == 3
+    assert reorder(m, cap=17) == 3
     assert reorder(m, W=0) == 0
 
 
@@ -110,6 +140,7 @@ def test_topk_errors(m):
     assert topk(m, kl=1025, V=5000) == 3
     assert topk(m, V=200000) == 3
     assert topk(m, W=2000) == 3
+    assert topk(m, W=513, kg=4) == 3
     assert topk(m, tok=None) == 1
     assert topk(m, wsb=16) == 5
     assert topk(m, ws=None) == 5

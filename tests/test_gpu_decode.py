@@ -21,17 +21,16 @@ def dev(c):
     return [t.to(DEV) for t in (c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v)]
 
 
-def check_decode(c, ls, name, reqs=None, scale=None):
+def check_decode(c, ls, name, scale=None):
+    """GPU decode of every request, then the oracle over every request, beam and head, element by element."""
     q, pk, pv, sk, sv = dev(c)
     say(f"[decode] {name} R={c.r} W={c.w} Lp={c.lp} Ls={ls}/{c.ls_cap} nq={c.nq} nkv={c.nkv} d={c.d}")
     out, lse = bga().shared_prefix_decode(q, pk, pv, sk, sv, ls, scale)
     torch.cuda.synchronize()
-    reqs = list(range(c.r)) if reqs is None else reqs
-    sl = slice(None)
-    ro, rl = oracle.shared_prefix_decode(c.q[reqs], c.prefix_k[reqs], c.prefix_v[reqs], c.suffix_k[reqs],
-                                         c.suffix_v[reqs], ls, scale)
-    e = check_bf16(out[reqs], ro, f"{name} out")
-    l = check_lse(lse[reqs], rl, f"{name} lse")
+    host = [t.cpu() for t in (c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v)]
+    ro, rl = oracle.shared_prefix_decode(*host, ls, scale)
+    e = check_bf16(out, ro, f"{name} out")
+    l = check_lse(lse, rl, f"{name} lse")
     say(f"    max |out err| {e:.2e}  max |lse err| {l:.2e}")
     return out, lse
 
@@ -42,12 +41,10 @@ def test_short_decode_config(ls):
     check_decode(c, ls, "short_decode")
 
 
-@pytest.mark.parametrize("ls", [1, 5])
-def test_long_beam_decode_config_sampled(ls):
+@pytest.mark.parametrize("ls", [1, 2, 3, 4, 5])
+def test_long_beam_decode_config_full(ls):
     c = wl.make_named_decode("long_beam", device=DEV)
-    for f in ("q", "prefix_k", "prefix_v", "suffix_k", "suffix_v"):
-        setattr(c, f, getattr(c, f).cpu())
-    check_decode(c, ls, "long_beam", reqs=[0, 5])
+    check_decode(c, ls, "long_beam")
 
 
 @pytest.mark.parametrize("r,w,lp,ls,cap,nq,nkv,d", [
@@ -59,6 +56,8 @@ def test_long_beam_decode_config_sampled(ls):
     (1, 33, 1, 1, 1, 3, 1, 64),      # prefix of one token
     (2, 100, 70, 3, 4, 8, 8, 64),    # group 1: up to 128 beams per workgroup (suffix rows in two slots)
     (1, 130, 64, 2, 2, 4, 4, 128),   # group 1, a full and a ragged workgroup, one prompt tile
+    (2, 512, 100, 16, 16, 16, 8, 64),   # the caps: 512 beams, 16 suffix positions
+    (1, 512, 33, 16, 16, 4, 4, 128),    # the caps with group 1 (128 beams per workgroup)
 ])
 def test_decode_edge_shapes(r, w, lp, ls, cap, nq, nkv, d):
     c = wl.make_decode_case(r, w, lp, cap, nq, nkv, d, seed=r * 1000 + w + lp)
@@ -97,6 +96,18 @@ def test_decode_determinism_and_beam_permutation():
 
 
 # ---------------------------------------------------------------- reorder
+
+def test_reorder_at_the_caps():
+    """512 beams, 16 suffix positions (BGA_MAX_BEAMS, BGA_MAX_SUFFIX), with token history."""
+    c = wl.make_decode_case(2, 512, 1, 16, 16, 8, 128, seed=512)
+    parent = wl.make_parents(2, 512, 512, seed=513)
+    tok = np.random.default_rng(514).integers(0, 151936, (2, 512, 16)).astype(np.int32)
+    dk, dv, dt = bga().suffix_reorder(c.suffix_k.to(DEV), c.suffix_v.to(DEV), torch.from_numpy(parent).to(DEV), 16,
+                                      src_tokens=torch.from_numpy(tok).to(DEV), num_tokens=16)
+    rk, rv, rt = oracle.suffix_reorder(c.suffix_k, c.suffix_v, parent, 16, tok, 16)
+    assert np.array_equal(wl.bf16_bits(dk.cpu()), rk) and np.array_equal(wl.bf16_bits(dv.cpu()), rv)
+    assert np.array_equal(dt.cpu().numpy(), rt)
+
 
 @pytest.mark.parametrize("name,ls", [("short_decode", 4), ("long_beam", 5), ("long_beam", 1)])
 def test_reorder_config_bit_exact(name, ls):

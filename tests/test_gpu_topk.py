@@ -6,8 +6,13 @@ the oracle's (fp64, rounded to fp32). Where that floating-point value decides
 the integer results, both sides decide from the same value: the oracle run
 with the GPU's row log-sum-exp must match every output bit for bit. Against
 the oracle's own log-sum-exp, a request may differ only where a row's GPU value
-differs from the oracle's fp32 value, and the GPU result must still be exactly
-the (-score, flat index) top-k of the GPU's own stage-1 scores.
+differs from the oracle's fp32 value, and then only at the cut: every candidate
+that one side selects and the other does not must score within 4 fp32 ulp of
+the oracle's k_global-th score (and every candidate's GPU score within 4 ulp of
+its oracle score), ulps taken at the larger of the score's and the row
+log-sum-exp's magnitude (the score inherits the log-sum-exp's rounding). The GPU result must also be exactly the (-score, flat index)
+top-k of the GPU's own stage-1 scores. The number of differing requests and the
+largest gap at the cut are printed.
 """
 import numpy as np
 import pytest
@@ -15,7 +20,7 @@ import torch
 
 import oracle
 import workloads as wl
-from helpers import say
+from helpers import CUT_GAP_ULP, cut_gap, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +65,7 @@ def run_and_check(x, cum, k_local, k_global, name):
     same_lse = oracle.beam_topk(x.cpu(), cum, k_local, k_global, row_lse=glse)
     for key in ("local_tokens", "local_scores", "tokens", "parents", "scores"):
         assert np.array_equal(res[key].cpu().numpy(), same_lse[key]), f"{key} differ given the same row lse"
-    n_mismatch = 0
+    n_mismatch, worst_gap, worst_drift = 0, 0, 0
     for i in range(x.shape[0]):
         same = (np.array_equal(res["tokens"][i].cpu().numpy(), ref["tokens"][i])
                 and np.array_equal(res["parents"][i].cpu().numpy(), ref["parents"][i])
@@ -68,9 +73,14 @@ def run_and_check(x, cum, k_local, k_global, name):
         if not same:
             n_mismatch += 1
             assert lse_diff[i].any(), f"request {i}: selection differs with identical row lse"
+            gap, drift = cut_gap({k: t.cpu().numpy() for k, t in res.items()}, ref, i, k_local, k_global)
+            assert drift <= CUT_GAP_ULP, f"request {i}: a candidate's GPU score is {drift:.2f} ulp from the oracle's"
+            assert gap <= CUT_GAP_ULP, f"request {i}: a candidate {gap:.2f} ulp from the cut is selected differently"
+            worst_gap, worst_drift = max(worst_gap, gap), max(worst_drift, drift)
         self_consistent(res, i, k_local, k_global)
     say(f"    rows with lse != oracle fp32: {int(lse_diff.sum())}/{lse_diff.size}; max |lse err| {lerr.max():.2e};"
-        f" requests differing: {n_mismatch}")
+        f" requests differing from the oracle's own lse: {n_mismatch}/{x.shape[0]}"
+        f" (largest gap at the cut {worst_gap:.2f} ulp, largest score drift {worst_drift:.2f} ulp)")
     return res, ref
 
 
@@ -120,6 +130,13 @@ def test_long_beam_config_full():
     x = wl.make_logits(cfg["r"], cfg["w"], cfg["vocab"], cfg["logit_std"], seed=cfg["seed"] + 1, device=DEV).cpu()
     cum = (np.random.default_rng(0).standard_normal((cfg["r"], cfg["w"])) * 3 - 20).astype(np.float32)
     run_and_check(x, cum, 2 * cfg["w"], cfg["w"], "long_beam")
+
+
+def test_caps_512_beams_k_1024():
+    """BGA_MAX_BEAMS source beams, k_local = k_global = BGA_MAX_K (2W global candidates at W = 512)."""
+    x = wl.make_logits(1, 512, 151936, 3.0, seed=512, device=DEV).cpu()
+    cum = (np.random.default_rng(512).standard_normal((1, 512)) - 10).astype(np.float32)
+    run_and_check(x, cum, 1024, 1024, "caps W=512 k=1024")
 
 
 def test_determinism():
