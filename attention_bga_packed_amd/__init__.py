@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     RELEASE_LIB_PATH,
     beam_topk,
+    beam_topk_noalloc,
     beam_topk_workspace_size,
     lib,
     load_library,

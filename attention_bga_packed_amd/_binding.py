@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "BGA_OK", 1: "BGA_ERR_NULL", 2: "BGA_ERR_SHAPE", 3: "BGA_ERR_
 # Every symbol declared in include/bga.h.
 EXPORTS = ("bga_packed_gqa_prefill", "bga_shared_prefix_decode", "bga_suffix_reorder",
            "bga_beam_topk_workspace_size", "bga_beam_topk", "bga_status_string", "bga_last_hip_error",
-           "bga_version", "bga_debug_build", "bga_last_violations")
+           "bga_version", "bga_debug_build", "bga_last_violations", "bga_beam_topk_noalloc")
 
 
 class BgaError(RuntimeError):
@@ -51,6 +51,7 @@ def load_library(path: str = LIB_PATH):
     L.bga_beam_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.bga_beam_topk_workspace_size.restype = sz
     L.bga_beam_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
+    L.bga_beam_topk_noalloc.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
     L.bga_status_string.argtypes = [i32]
     L.bga_status_string.restype = ctypes.c_char_p
     L.bga_last_hip_error.argtypes = []
@@ -59,7 +60,7 @@ def load_library(path: str = LIB_PATH):
     L.bga_last_violations.argtypes = []
     L.bga_last_violations.restype = ctypes.c_uint32
     for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_suffix_reorder, L.bga_beam_topk,
-              L.bga_last_hip_error, L.bga_version, L.bga_debug_build):
+              L.bga_beam_topk_noalloc, L.bga_last_hip_error, L.bga_version, L.bga_debug_build):
         f.restype = i32
     return L
 
@@ -201,19 +202,13 @@ def beam_topk_workspace_size(num_requests, num_src_beams, vocab, k_local, k_glob
     return int(lib.bga_beam_topk_workspace_size(num_requests, num_src_beams, vocab, k_local, k_global))
 
 
-def beam_topk(logits, cum_scores, k_local: int, k_global: int, workspace=None, want_local: bool = False,
-              want_lse: bool = False, out=None):
-    """Two-stage beam candidate selection. logits [R,W_in,V] bf16; cum_scores [R,W_in] fp32 or None.
-    Returns dict(tokens, parents, scores[, local_tokens, local_scores][, row_lse])."""
+def _topk_outputs(logits, cum_scores, k_local, k_global, want_local, want_lse, out):
+    """Checked (and, where missing, allocated) output tensors of a beam top-K call."""
     _need(logits, "logits", torch.bfloat16, ndim=3)
     dev = logits.device
     r, w_in, vocab = logits.shape
     if cum_scores is not None:
         _need(cum_scores, "cum_scores", torch.float32, dev, shape=(r, w_in))
-    need = beam_topk_workspace_size(r, w_in, vocab, k_local, k_global)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, dev, 1)
     res = out if out is not None else {}
     shapes = {"tokens": ((r, k_global), torch.int32), "parents": ((r, k_global), torch.int32),
               "scores": ((r, k_global), torch.float32)}
@@ -229,9 +224,42 @@ def beam_topk(logits, cum_scores, k_local: int, k_global: int, workspace=None, w
         if key not in res:
             res[key] = torch.empty(shape, dtype=dtype, device=dev)
         _need(res[key], key, dtype, dev, shape=shape)
+    return res
+
+
+def beam_topk(logits, cum_scores, k_local: int, k_global: int, workspace=None, want_local: bool = False,
+              want_lse: bool = False, out=None):
+    """Two-stage beam candidate selection. logits [R,W_in,V] bf16; cum_scores [R,W_in] fp32 or None.
+    Returns dict(tokens, parents, scores[, local_tokens, local_scores][, row_lse])."""
+    res = _topk_outputs(logits, cum_scores, k_local, k_global, want_local, want_lse, out)
+    r, w_in, vocab = logits.shape
+    need = beam_topk_workspace_size(r, w_in, vocab, k_local, k_global)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=logits.device)
+    _need(workspace, "workspace", torch.uint8, logits.device, 1)
     st = lib.bga_beam_topk(_ptr(logits), _ptr(cum_scores), r, w_in, vocab, int(k_local), int(k_global),
                            _ptr(res["tokens"]), _ptr(res["parents"]), _ptr(res["scores"]),
                            _ptr(res.get("local_tokens")), _ptr(res.get("local_scores")), _ptr(res.get("row_lse")),
                            _ptr(workspace), workspace.numel(), _stream(logits))
     _check(st, "bga_beam_topk")
+    return res
+
+
+def beam_topk_noalloc(logits, cum_scores, k_local: int, k_global: int, out: dict, want_local: bool = False,
+                      want_lse: bool = False):
+    """bga_beam_topk_noalloc: beam_topk with the library's own per-device workspace. Every output tensor
+    must be passed in `out` (tokens, parents, scores, and local_tokens/local_scores/row_lse when wanted):
+    nothing is allocated on this path."""
+    r, w_in, vocab = logits.shape
+    keys = {"tokens", "parents", "scores"} | ({"local_tokens", "local_scores"} if want_local else set()) | \
+        ({"row_lse"} if want_lse else set())
+    missing = keys - set(out)
+    if missing:
+        raise ValueError(f"beam_topk_noalloc allocates nothing: pass {sorted(missing)} in out")
+    res = _topk_outputs(logits, cum_scores, k_local, k_global, want_local, want_lse, out)
+    st = lib.bga_beam_topk_noalloc(_ptr(logits), _ptr(cum_scores), r, w_in, vocab, int(k_local), int(k_global),
+                                   _ptr(res["tokens"]), _ptr(res["parents"]), _ptr(res["scores"]),
+                                   _ptr(res.get("local_tokens")), _ptr(res.get("local_scores")),
+                                   _ptr(res.get("row_lse")), _stream(logits))
+    _check(st, "bga_beam_topk_noalloc")
     return res

@@ -181,31 +181,71 @@ size_t bga_beam_topk_workspace_size(int32_t num_requests, int32_t num_src_beams,
     return bga::topk_workspace_layout(num_requests, num_src_beams, k_local).total;
 }
 
-bga_status bga_beam_topk(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
-                         int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
-                         int32_t *out_tokens, int32_t *out_parents, float *out_scores, int32_t *local_tokens,
-                         float *local_scores, float *row_lse, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream)
+// Host checks shared by both top-K entry points; *need = workspace bytes.
+static bga_status topk_check(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
+                             int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
+                             int32_t *out_tokens, int32_t *out_parents, float *out_scores, int32_t *local_tokens,
+                             float *local_scores, float *row_lse, size_t *need)
 {
+    *need = 0;
     if (num_requests < 0 || num_src_beams <= 0 || vocab <= 0 || k_local <= 0 || k_global <= 0)
         return BGA_ERR_SHAPE;
     if ((int64_t)k_global > (int64_t)num_src_beams * k_local || k_local > vocab) return BGA_ERR_SHAPE;
     if (!topk_sizes_ok(num_requests, num_src_beams, vocab, k_local, k_global)) return BGA_ERR_UNSUPPORTED;
     if (num_requests == 0) return BGA_OK;
     if (!logits || !out_tokens || !out_parents || !out_scores) return BGA_ERR_NULL;
-    const size_t need = bga::topk_workspace_layout(num_requests, num_src_beams, k_local).total;
-    if (!workspace || workspace_bytes < need) return BGA_ERR_WORKSPACE;
-    if (!aligned(logits, 16) || !aligned(workspace, 16) || !aligned(out_tokens, 4) || !aligned(out_parents, 4) ||
-        !aligned(out_scores, 4) || (cum_scores && !aligned(cum_scores, 4)) ||
-        (local_tokens && !aligned(local_tokens, 4)) || (local_scores && !aligned(local_scores, 4)) ||
-        (row_lse && !aligned(row_lse, 4)))
+    if (!aligned(logits, 16) || !aligned(out_tokens, 4) || !aligned(out_parents, 4) || !aligned(out_scores, 4) ||
+        (cum_scores && !aligned(cum_scores, 4)) || (local_tokens && !aligned(local_tokens, 4)) ||
+        (local_scores && !aligned(local_scores, 4)) || (row_lse && !aligned(row_lse, 4)))
         return BGA_ERR_ALIGN;
+    *need = bga::topk_workspace_layout(num_requests, num_src_beams, k_local).total;
+    return BGA_OK;
+}
+
+bga_status bga_beam_topk(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
+                         int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
+                         int32_t *out_tokens, int32_t *out_parents, float *out_scores, int32_t *local_tokens,
+                         float *local_scores, float *row_lse, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream)
+{
+    size_t need = 0;
+    bga_status st = topk_check(logits, cum_scores, num_requests, num_src_beams, vocab, k_local, k_global,
+                               out_tokens, out_parents, out_scores, local_tokens, local_scores, row_lse, &need);
+    if (st != BGA_OK || num_requests == 0) return st;
+    if (!workspace || workspace_bytes < need) return BGA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return BGA_ERR_ALIGN;
     const size_t lbytes = (size_t)num_requests * num_src_beams * vocab * 2;
     if (overlap(workspace, need, logits, lbytes)) return BGA_ERR_ALIAS;
 #ifdef BGA_DEBUG
     {
         uint32_t bad = 0;
-        const bga_status st = check_status(bga::debug_check_logits(logits, lbytes / 2, stream, &bad), bad);
+        st = check_status(bga::debug_check_logits(logits, lbytes / 2, stream, &bad), bad);
+        if (st != BGA_OK) return st;
+    }
+#endif
+    return hip_status(bga::launch_beam_topk(logits, cum_scores, num_requests, num_src_beams, vocab, k_local,
+                                            k_global, out_tokens, out_parents, out_scores, local_tokens,
+                                            local_scores, row_lse, workspace, stream));
+}
+
+bga_status bga_beam_topk_noalloc(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
+                                 int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
+                                 int32_t *out_tokens, int32_t *out_parents, float *out_scores,
+                                 int32_t *local_tokens, float *local_scores, float *row_lse, hipStream_t stream)
+{
+    size_t need = 0;
+    bga_status st = topk_check(logits, cum_scores, num_requests, num_src_beams, vocab, k_local, k_global,
+                               out_tokens, out_parents, out_scores, local_tokens, local_scores, row_lse, &need);
+    if (st != BGA_OK || num_requests == 0) return st;
+    if (need > BGA_TOPK_SCRATCH_BYTES) return BGA_ERR_WORKSPACE;
+    void *workspace = nullptr;
+    hipError_t e = bga::topk_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e);
+#ifdef BGA_DEBUG
+    {
+        uint32_t bad = 0;
+        const size_t lbytes = (size_t)num_requests * num_src_beams * vocab * 2;
+        st = check_status(bga::debug_check_logits(logits, lbytes / 2, stream, &bad), bad);
         if (st != BGA_OK) return st;
     }
 #endif

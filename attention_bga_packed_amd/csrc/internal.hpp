@@ -31,6 +31,10 @@ struct TopkWorkspace {
 };
 TopkWorkspace topk_workspace_layout(int R, int W_in, int k_local);
 
+// Device address of the current device's BGA_TOPK_SCRATCH_BYTES of library-owned
+// top-K workspace (looked up once per device, then cached).
+hipError_t topk_scratch(void **ptr);
+
 hipError_t launch_beam_topk(const uint16_t *logits, const float *cum, int R, int W_in, int V, int k_local,
                             int k_global, int32_t *out_tok, int32_t *out_par, float *out_score,
                             int32_t *local_tok, float *local_score, float *row_lse, void *workspace,

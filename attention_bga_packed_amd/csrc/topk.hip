@@ -41,6 +41,9 @@
 // of 64 sorted in registers by binary searches. When too many
 // entries are >= L (many equal scores), the exact cut comes from radix selects
 // over the beams' prefixes instead, ties by lower flat index.
+#include <mutex>
+
+#include "bga.h"
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -1095,6 +1098,38 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
             out_score[(size_t)r * k_global + place] = ws_score[src];
         }
     }
+}
+
+// The library's own workspace for callers that cannot allocate device memory
+// (bga_beam_topk_noalloc): one array per device, in the code object's
+// zero-initialised data, held from the module's load until the process ends.
+// Host code never uses the array's name as an address (on the host it is a
+// stand-in, not device memory): topk_scratch() looks up each device's copy
+// once, with that device current, and every later use goes through that
+// pointer. Stage 1 writes every entry stage 2 reads, so nothing is cleared.
+static __device__ __align__(256) unsigned char scratch[BGA_TOPK_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t topk_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 TopkWorkspace topk_workspace_layout(int R, int W_in, int k_local)

@@ -184,6 +184,30 @@ bga_status bga_beam_topk(const bga_bf16 *logits, const float *cum_scores, int32_
                          float *local_scores, float *row_lse, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* Size of the library's own per-device top-K workspace used by
+ * bga_beam_topk_noalloc. */
+#define BGA_TOPK_SCRATCH_BYTES ((size_t)24 << 20)
+
+/*
+ * bga_beam_topk for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the same
+ * operation, arguments and results, with the stage-1 lists kept in a workspace
+ * the library owns instead of a caller-provided one. No allocation of any kind
+ * happens in this call; the caller still passes every input and output.
+ *
+ * The workspace is one array of BGA_TOPK_SCRATCH_BYTES per device, resident
+ * from the library's first use on that device until the process ends. Sizes
+ * whose bga_beam_topk_workspace_size() exceeds it return BGA_ERR_WORKSPACE
+ * (8 x 400 source beams with k_local = 800 need 20.5 MB and fit). Every call on
+ * one device shares that array: calls that overlap on one device (different
+ * streams, or host threads) race and must be serialised by the caller; calls
+ * on different devices do not interact.
+ */
+bga_status bga_beam_topk_noalloc(const bga_bf16 *logits, const float *cum_scores, int32_t num_requests,
+                                 int32_t num_src_beams, int32_t vocab, int32_t k_local, int32_t k_global,
+                                 int32_t *out_tokens, int32_t *out_parents, float *out_scores,
+                                 int32_t *local_tokens, float *local_scores, float *row_lse, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *bga_status_string(bga_status s);
 

@@ -146,3 +146,15 @@ def test_topk_errors(m):
     assert topk(m, ws=None) == 5
     assert topk(m, logits=P + 2) == 4
     assert topk(m, R=0) == 0
+
+
+def test_topk_noalloc_errors(m):
+    def na(R=2, W=4, V=1000, kl=8, kg=4, logits=P, tok=2 * P):
+        return m.lib.bga_beam_topk_noalloc(logits, None, R, W, V, kl, kg, tok, 3 * P, 4 * P, None, None, None, None)
+    assert na(kl=2000) == 2
+    assert na(tok=None) == 1
+    assert na(logits=P + 2) == 4
+    assert na(R=0) == 0
+    # the library's own workspace holds 24 MiB: 8 x 400 beams with k_local 800 fit, 8 x 512 x 1024 do not
+    assert m.beam_topk_workspace_size(8, 400, 151936, 800, 400) <= 24 << 20
+    assert na(R=8, W=512, V=151936, kl=1024, kg=1024) == 5
