@@ -1,29 +1,41 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one pass of the whole hot path over synthetic inputs:
-  * a Prefill-Only request: 28 launches (one per layer) of packed causal GQA
-    prefill over 15 packed sequences, lengths uniform in [64, 480] (T = 4228),
-    16 query / 8 KV heads, head dim 128, each layer with its own Q/K/V;
-  * a long-prompt beam search: 8 requests x 400 beams over a 480-token shared
-    prompt, 5 decode steps, each = shared-prefix decode (16/8 heads, d 128,
-    suffix length = step) -> two-stage top-K over bf16 logits [8, 400, 151936]
-    (2W per beam, W overall) -> parent-index suffix K/V reorder.
+One step = one pass of the whole hot path over one batch of synthetic input of
+every measured workload:
+  * Prefill-Only request: 28 launches (one per layer, each with its own Q/K/V)
+    of packed causal GQA prefill over 15 sequences, lengths uniform in
+    [64, 480] (T = 4228), 16 query / 8 KV heads, head dim 128;
+  * long packed prefill: 120 sequences, lognormal lengths (median 400,
+    sigma 0.4, clipped to [32, 1024]; T = 52,348), 14 / 2 heads, head dim 64;
+  * long packed prefill, 120 x 1024 tokens (T = 122,880), 14 / 2 heads, d 64;
+  * short-prompt beam decode: 32 requests x 100 beams over a 128-token shared
+    prompt, 4 steps of shared-prefix decode (16 / 8 heads, d 64, suffix length
+    = step) + parent-index suffix reorder (parents drawn uniformly);
+  * long-prompt beam search: 8 requests x 400 beams over a 480-token prompt,
+    5 steps of shared-prefix decode (16 / 8 heads, d 128) -> two-stage top-K
+    over bf16 logits [8, 400, 151936] (2W per beam, W overall) -> reorder.
 
-The headline value is the prefill attention throughput in logical TFLOP/s
-(4 * D * Nq * sum L(L+1)/2 per layer, FMA = 2); decode, top-K and reorder are
-reported in algorithmic GB/s. Kernel times come from HIP events on the launching
-stream around launches that run back to back behind a spin gate: one pair around
-the 28 prefill launches of a request (the average launch is their span / 28), and
-for decode, top-K and reorder one pair around K repeats of each step's launch.
-Inputs are drawn on the GPU from fixed seeds.
-Prints one JSON line.
+The headline value is the prefill attention throughput on the 120 x 1024 batch,
+the one prefill workload whose arithmetic intensity (442 FLOP/B) is above the
+MI355X ridge (2500 TFLOP/s / 8 TB/s = 312.5 FLOP/B), in logical TFLOP/s
+(4 * D * Nq * sum L(L+1)/2, FMA = 2), with its roofline against the bf16 MFMA
+peak. `rooflines` holds every kernel and workload: prefill in TFLOP/s and
+algorithmic GB/s (bound by the intensity), decode, top-K and reorder in
+algorithmic GB/s. Kernel durations come from HIP events on the launching
+stream around launches that run back to back behind a spin gate, rotating over
+input sets that together exceed the 256 MB Infinity Cache. `cpu_baseline`
+times the fp64 oracle on the headline workload on the host cores (median of
+three); `cpu_baselines` does the same for every operation on bounded samples.
+Inputs are drawn on the GPU from fixed seeds and are resident in HBM before
+any timing. Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -32,12 +44,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP/B
+METRIC = "attention TFLOPS & %bf16 MFMA peak (prefill); GB/s & %HBM peak (beam decode)"
 
 # HBM bytes per launch, from two rocprofv3 --pmc passes over this script (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch, averaged over the kernel's dispatches). Calibration: a plain 512 MiB
-# device copy (--calib-copy-mb 512) reads FETCH_SIZE = 262156 KiB and WRITE_SIZE = 524288 KiB, so
-# fetch counts are scaled by 2 and write counts by 1 (beam_topk: both of its kernels). Each figure is tied to the sources of the
-# kernel it was measured on and is reported as null once they change.
+# WRITE_SIZE, KiB per dispatch, averaged over the workload's dispatches). Calibration: a plain
+# 512 MiB device copy (--calib-copy-mb 512) reads FETCH_SIZE = 262156 KiB and WRITE_SIZE =
+# 524288 KiB, so fetch counts are scaled by 2 and write counts by 1. Each figure is tied to a
+# hash of the sources of the kernel it was measured on and is reported as null once they change.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {
     "packed_gqa_prefill": ["prefill.hip", "attn_core.hpp", "device_common.hpp", "internal.hpp"],
@@ -45,12 +59,8 @@ KERNEL_SOURCES = {
     "beam_topk": ["topk.hip", "device_common.hpp", "internal.hpp"],
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
 }
-MEASURED_TRAFFIC = {
-    "packed_gqa_prefill": {"fetch_kib": 17173.9, "write_kib": 17972.2, "sources_sha256": "63a7f5e4487d387a"},
-    "shared_prefix_decode": {"fetch_kib": 34130.2, "write_kib": 14944.1, "sources_sha256": "35756fe22eeed70b"},
-    "beam_topk": {"fetch_kib": 487023.4, "write_kib": 20037.5, "sources_sha256": "387ba3c5334eb011"},
-    "suffix_reorder": {"fetch_kib": 14882.8, "write_kib": 38400.0, "sources_sha256": "8c1e96f48115f389"},
-}
+# workload -> {"kernel", "fetch_kib", "write_kib", "sources_sha256"}
+MEASURED_TRAFFIC: dict = {}
 
 
 def sources_sha(kernel):
@@ -62,10 +72,10 @@ def sources_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
+def measured_traffic(workload):
     """Counter-derived HBM bytes per launch, or None if not measured on the current sources."""
-    t = MEASURED_TRAFFIC.get(kernel)
-    if t is None or t["sources_sha256"] != sources_sha(kernel):
+    t = MEASURED_TRAFFIC.get(workload)
+    if t is None or t["sources_sha256"] != sources_sha(t["kernel"]):
         return None
     return int(round(t["fetch_kib"] * 1024 * FETCH_SCALE + t["write_kib"] * 1024 * WRITE_SCALE))
 
@@ -75,15 +85,186 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="CPU time budget for the oracle baseline sample (0 disables it)")
-    ap.add_argument("--only", choices=["long_prefill", "long_prefill_1024", "short_decode"], default=None,
-                    help="instead of the step, time one other configuration by itself (its kernel launched back "
-                         "to back) and print a JSON line for it")
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="scale of the oracle baselines (0 disables them; 1 = the default samples, ~15 s)")
+    ap.add_argument("--only", choices=["prefill_only", "long_prefill", "long_prefill_1024", "short_decode",
+                                       "long_beam"], default=None,
+                    help="run (and time) only this workload's launches; for profiling one workload")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size dispatch "
                          "for calibrating the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+class Timer:
+    """Average duration of back-to-back launches: HIP events on the launching stream around n calls,
+    queued behind a spin kernel that holds the GPU while the host enqueues them (so the host's
+    per-launch overhead is not counted)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        torch.cuda._sleep(1 << 20)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        self.cycles_per_ms = (1 << 20) / max(a.elapsed_time(b), 1e-3)
+
+    def span_ms(self, fns, n):
+        """Total ms of n back-to-back calls cycling over fns (host enqueue hidden behind a gate)."""
+        torch = self.torch
+        fns[0]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(self.cycles_per_ms * max(3.0 * host_ms, 2.0)))
+        a.record(self.stream)
+        for i in range(n):
+            fns[i % len(fns)]()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+
+def build_inputs(dev, only=None):
+    """Every workload's inputs and launch closures, resident in HBM. Returns {workload: dict}."""
+    W = {}
+    for name, make in (("prefill_only", lambda: prefill_workload("prefill_only", None, dev)),
+                       ("long_prefill", lambda: prefill_workload("long_prefill", 3, dev)),
+                       ("long_prefill_1024", lambda: prefill_workload("long_prefill_1024", 2, dev)),
+                       ("short_decode", lambda: short_decode_workload(dev)),
+                       ("long_beam", lambda: long_beam_workload(dev))):
+        if only is None or only == name:
+            W[name] = make()
+    return W
+
+
+def prefill_workload(name, nsets, dev):
+    """One input set per launch of a step (Prefill-Only: one per layer); the long batches have several
+    sets, rotated when timed so that together they exceed the Infinity Cache."""
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import workloads as wl
+
+    cfg = wl.CONFIGS[name]
+    lengths = wl.prefill_lengths(cfg)
+    n = cfg.get("layers", nsets)
+    cases = [wl.make_prefill_case(lengths, cfg["nq"], cfg["nkv"], cfg["d"], cfg["seed"] * 1000 + i, dev)
+             for i in range(n)]
+    cu = torch.from_numpy(cases[0].cu_seqlens).to(dev)
+    out = torch.empty_like(cases[0].q)
+    lse = torch.empty(cases[0].q.shape[:2], dtype=torch.float32, device=dev)
+    mx = max(lengths)
+    fns = [lambda c=c: bga.packed_gqa_prefill(c.q, c.k, c.v, cu, mx, out=out, lse=lse) for c in cases]
+    return dict(kind="prefill", cfg=cfg, lengths=lengths, cases=cases, fns=fns,
+                step_launches=fns if name == "prefill_only" else fns[:1])
+
+
+def short_decode_workload(dev):
+    """4 steps of shared-prefix decode + reorder with parents drawn uniformly (no top-K in this workload)."""
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import workloads as wl
+
+    cfg = wl.CONFIGS["short_decode"]
+    R, Wb, LP, NS = cfg["r"], cfg["w"], cfg["lp"], cfg["steps"]
+    sets = [wl.make_decode_case(R, Wb, LP, cfg["ls_cap"], cfg["nq"], cfg["nkv"], cfg["d"], cfg["seed"] * 1000 + i,
+                                dev) for i in range(4)]
+    parents = [torch.from_numpy(wl.make_parents(R, Wb, Wb, cfg["seed"] + 10 * s)).to(dev) for s in range(NS)]
+    out = torch.empty_like(sets[0].q)
+    lse = torch.empty(sets[0].q.shape[:3], dtype=torch.float32, device=dev)
+    bufs = [(sets[0].suffix_k, sets[0].suffix_v), (torch.empty_like(sets[0].suffix_k),
+                                                     torch.empty_like(sets[0].suffix_v))]
+
+    def step():
+        cur = 0
+        for s in range(NS):
+            sk, sv = bufs[cur]
+            bga.shared_prefix_decode(sets[0].q, sets[0].prefix_k, sets[0].prefix_v, sk, sv, s + 1, out=out, lse=lse)
+            bga.suffix_reorder(sk, sv, parents[s], s + 1, dst_k=bufs[1 - cur][0], dst_v=bufs[1 - cur][1])
+            cur = 1 - cur
+
+    dec = [[lambda c=c, s=s: bga.shared_prefix_decode(c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, s + 1,
+                                                      out=out, lse=lse) for c in sets] for s in range(NS)]
+    reo = [[lambda c=c, s=s: bga.suffix_reorder(c.suffix_k, c.suffix_v, parents[s], s + 1, dst_k=bufs[1][0],
+                                                dst_v=bufs[1][1]) for c in sets] for s in range(NS)]
+    return dict(kind="beam", cfg=cfg, sets=sets, parents=parents, step=step, decode=dec, reorder=reo)
+
+
+def long_beam_workload(dev):
+    """5 steps of shared-prefix decode -> two-stage top-K -> reorder by the selected parents."""
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import workloads as wl
+
+    cfg = wl.CONFIGS["long_beam"]
+    R, Wb, LP, NS, NQ, NKV, D, V = (cfg[k] for k in ("r", "w", "lp", "steps", "nq", "nkv", "d", "vocab"))
+    sets = [wl.make_named_decode("long_beam", device=dev)] + [
+        wl.make_decode_case(R, Wb, LP, NS, NQ, NKV, D, cfg["seed"] * 1000 + i, dev) for i in range(1, 4)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg["seed"] * 7919)
+    qs = [wl.bf16_normal((R, Wb, NQ, D), gen, dev) for _ in range(NS)]
+    logits = [wl.make_logits(R, Wb, V, cfg["logit_std"], cfg["seed"] + s + 1, dev) for s in range(NS)]
+    dc = sets[0]
+    bufs = [(dc.suffix_k, dc.suffix_v), (torch.empty_like(dc.suffix_k), torch.empty_like(dc.suffix_v))]
+    out = torch.empty_like(qs[0])
+    lse = torch.empty((R, Wb, NQ), dtype=torch.float32, device=dev)
+    ws = torch.empty(bga.beam_topk_workspace_size(R, Wb, V, 2 * Wb, Wb), dtype=torch.uint8, device=dev)
+    tk = {"tokens": torch.empty((R, Wb), dtype=torch.int32, device=dev),
+          "parents": torch.empty((R, Wb), dtype=torch.int32, device=dev),
+          "scores": torch.empty((R, Wb), dtype=torch.float32, device=dev)}
+    cum = torch.zeros((R, Wb), dtype=torch.float32, device=dev)
+
+    def step():
+        cur = 0
+        cum.zero_()
+        for s in range(NS):
+            sk, sv = bufs[cur]
+            nk, nv = bufs[1 - cur]
+            bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=out, lse=lse)
+            bga.beam_topk(logits[s], cum, 2 * Wb, Wb, workspace=ws, out=tk)
+            bga.suffix_reorder(sk, sv, tk["parents"], s + 1, dst_k=nk, dst_v=nv)
+            cum.copy_(tk["scores"])
+            cur = 1 - cur
+
+    dec = [[lambda c=c, s=s: bga.shared_prefix_decode(c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, s + 1,
+                                                      out=out, lse=lse) for c in sets] for s in range(NS)]
+    reo = [[lambda c=c, s=s: bga.suffix_reorder(c.suffix_k, c.suffix_v, tk["parents"], s + 1, dst_k=bufs[1][0],
+                                                dst_v=bufs[1][1]) for c in sets] for s in range(NS)]
+    top = [lambda j=j: bga.beam_topk(logits[j], cum, 2 * Wb, Wb, workspace=ws, out=tk) for j in range(NS)]
+    return dict(kind="beam", cfg=cfg, sets=sets, step=step, decode=dec, reorder=reo, topk=top, logits=logits)
+
+
+def roof(bound, achieved, peak, unit, per_launch, ms, traffic):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "algorithmic_per_launch": per_launch,
+            "avg_launch_us": round(ms * 1e3, 2)}
+
+
+def prefill_roofline(name, w, ms):
+    import workloads as wl
+    cfg, lengths = w["cfg"], w["lengths"]
+    flops = wl.prefill_flops(lengths, cfg["nq"], cfg["d"])
+    hbm = wl.prefill_bytes(lengths, cfg["nq"], cfg["nkv"], cfg["d"])
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = hbm / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(name)
+    if flops / hbm >= RIDGE:
+        r = roof("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", flops, ms, traffic)
+    else:
+        r = roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", hbm, ms, traffic)
+    r.update({"kernel": "packed_prefill_kernel", "flop_per_byte": round(flops / hbm, 1), "tflops": round(tf, 2),
+              "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "gbs": round(gbs, 1),
+              "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_flops": flops, "algorithmic_bytes": hbm})
+    return r
 
 
 def main():
@@ -97,7 +278,6 @@ def main():
     import numpy as np
     import torch
 
-    import attention_bga_packed_amd as bga
     import workloads as wl
 
     dev = torch.device("cuda:0")
@@ -109,181 +289,88 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.only:
-        print(json.dumps(only_config(args, dev)), flush=True)
-        return
 
-    # ---------------- inputs (resident in HBM before timing)
-    pcfg = wl.CONFIGS["prefill_only"]
-    lengths = wl.prefill_lengths(pcfg)
-    layers = pcfg["layers"]
-    cases = [wl.make_prefill_case(lengths, pcfg["nq"], pcfg["nkv"], pcfg["d"], pcfg["seed"] * 1000 + i, dev)
-             for i in range(layers)]
-    cu = torch.from_numpy(cases[0].cu_seqlens).to(dev)
-    max_len = max(lengths)
-    p_out = torch.empty_like(cases[0].q)
-    p_lse = torch.empty(cases[0].q.shape[:2], dtype=torch.float32, device=dev)
-
-    bcfg = wl.CONFIGS["long_beam"]
-    R, W, LP, NS, NQ, NKV, D, V = (bcfg[k] for k in ("r", "w", "lp", "steps", "nq", "nkv", "d", "vocab"))
-    dc = wl.make_named_decode("long_beam", device=dev)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(bcfg["seed"] * 7919)
-    qs = [wl.bf16_normal((R, W, NQ, D), gen, dev) for _ in range(NS)]
-    logits = [wl.make_logits(R, W, V, bcfg["logit_std"], bcfg["seed"] + s + 1, dev) for s in range(NS)]
-    suf = [(dc.suffix_k, dc.suffix_v), (torch.empty_like(dc.suffix_k), torch.empty_like(dc.suffix_v))]
-    d_out = torch.empty_like(qs[0])
-    d_lse = torch.empty((R, W, NQ), dtype=torch.float32, device=dev)
-    ws = torch.empty(bga.beam_topk_workspace_size(R, W, V, 2 * W, W), dtype=torch.uint8, device=dev)
-    topk_out = {"tokens": torch.empty((R, W), dtype=torch.int32, device=dev),
-                "parents": torch.empty((R, W), dtype=torch.int32, device=dev),
-                "scores": torch.empty((R, W), dtype=torch.float32, device=dev)}
-    cum = torch.zeros((R, W), dtype=torch.float32, device=dev)
+    W = build_inputs(dev, args.only)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))]
-
-    def beam_launches(s, cur):
-        """The three launches of beam-search step s (suffix length s + 1), suffix buffers suf[cur] -> suf[1 - cur]."""
-        sk, sv = suf[cur]
-        nk, nv = suf[1 - cur]
-        return (
-            lambda: bga.shared_prefix_decode(qs[s], dc.prefix_k, dc.prefix_v, sk, sv, s + 1, out=d_out, lse=d_lse),
-            lambda: bga.beam_topk(logits[s], cum, 2 * W, W, workspace=ws, out=topk_out),
-            lambda: bga.suffix_reorder(sk, sv, topk_out["parents"], s + 1, dst_k=nk, dst_v=nv),
-        )
-
-    def step(timed):
-        """One pass of the hot path; with `timed`, one HIP event pair brackets the prefill layers."""
-        # the 28 layers run back to back, as in a request; one event pair spans them
-        if timed:
-            evs[0][0].record(stream)
-        for c in cases:
-            bga.packed_gqa_prefill(c.q, c.k, c.v, cu, max_len, out=p_out, lse=p_lse)
-        if timed:
-            evs[0][1].record(stream)
-        cur = 0
-        cum.zero_()
-        for s in range(NS):
-            for fn in beam_launches(s, cur):
-                fn()
-            cum.copy_(topk_out["scores"])
-            cur = 1 - cur
+    def step():
+        for name in ("prefill_only", "long_prefill", "long_prefill_1024"):
+            if name in W:
+                for fn in W[name]["step_launches"]:
+                    fn()
+        for name in ("short_decode", "long_beam"):
+            if name in W:
+                W[name]["step"]()
 
     for _ in range(args.warmup):
-        step(True)
+        step()
     torch.cuda.synchronize()
 
     # ---- timed region: K whole steps, wall clock
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    # ---- per-kernel durations: the same K steps again, HIP events on the launching stream. A spin
-    # kernel queued first holds the GPU while the host enqueues the whole step, so the launches run
-    # back to back and the event pairs span only the kernels (otherwise the host's per-launch
-    # overhead, which exceeds a prefill launch, would be counted too).
-    host_t = time.perf_counter()
-    step(True)
-    host_t = time.perf_counter() - host_t
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    torch.cuda._sleep(1 << 20)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
-    gate = int(cycles_per_ms * max(3.0 * host_t * 1e3, 2.0))
-
-    t_pre = 0.0
-    for _ in range(args.steps):
-        torch.cuda._sleep(gate)
-        step(True)
-        torch.cuda.synchronize()   # events of this step are complete; read them
-        t_pre += evs[0][0].elapsed_time(evs[0][1])
-
-    # Beam-search kernels, each timed by itself: K launches back to back behind the gate with one event
-    # pair around them (an event pair around one short launch would also count its dispatch gap), the
-    # launches rotating over input sets that together exceed the 256 MB Infinity Cache (four decode
-    # sets of 160 MB; the five 194 MB logits tensors). Average launch = span / K.
-    dsets = [dc] + [wl.make_decode_case(R, W, LP, NS, NQ, NKV, D, bcfg["seed"] * 1000 + i, dev) for i in range(1, 4)]
-    torch.cuda.synchronize()
-
-    def back_to_back(fns):
-        fns[0]()
-        torch.cuda.synchronize()
-        torch.cuda._sleep(gate)
-        evs[0][0].record(stream)
-        for i in range(args.steps):
-            fns[i % len(fns)]()
-        evs[0][1].record(stream)
-        torch.cuda.synchronize()
-        return evs[0][0].elapsed_time(evs[0][1])
-
-    t_dec, t_reo = [0.0] * NS, [0.0] * NS
-    for s in range(NS):
-        t_dec[s] = back_to_back([lambda ds=ds, s=s: bga.shared_prefix_decode(ds.q, ds.prefix_k, ds.prefix_v, ds.suffix_k,
-                                                                              ds.suffix_v, s + 1, out=d_out, lse=d_lse)
-                                 for ds in dsets])
-        t_reo[s] = back_to_back([lambda ds=ds, s=s: bga.suffix_reorder(ds.suffix_k, ds.suffix_v, topk_out["parents"],
-                                                                        s + 1, dst_k=suf[1][0], dst_v=suf[1][1])
-                                 for ds in dsets])
-    t_top = [back_to_back([lambda j=j: bga.beam_topk(logits[j], cum, 2 * W, W, workspace=ws, out=topk_out)
-                           for j in range(NS)])] * NS
-
     K = args.steps
-    pre_flops = wl.prefill_flops(lengths, pcfg["nq"], pcfg["d"])
-    pre_ms = t_pre / (K * layers)                           # average launch, ms
-    pre_tflops = pre_flops / (pre_ms * 1e-3) / 1e12
-    dec_bytes = [wl.decode_bytes(R, W, NQ, NKV, LP, s + 1, D) for s in range(NS)]
-    dec_ms = [t / K for t in t_dec]
-    dec_gbs = sum(dec_bytes) / (sum(dec_ms) * 1e-3) / 1e9
-    dec_flops = sum(wl.decode_flops(R, W, NQ, LP, s + 1, D) for s in range(NS))
-    top_bytes = wl.topk_bytes(R, W, V, W)
-    top_ms = sum(t_top) / (K * NS)
-    top_gbs = top_bytes / (top_ms * 1e-3) / 1e9
-    reo_bytes = [wl.reorder_bytes(R, W, s + 1, NKV, D) for s in range(NS)]
-    reo_ms = [t / K for t in t_reo]
-    reo_gbs = sum(reo_bytes) / (sum(reo_ms) * 1e-3) / 1e9
 
-    def roof(kernel, bound, achieved, peak, unit, per_launch, ms):
-        return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel),
-                "algorithmic_per_launch": per_launch, "avg_launch_us": round(ms * 1e3, 2)}
+    # ---- per-kernel durations (events around back-to-back launches, inputs rotated)
+    timer = Timer(torch)
+    rooflines, detail = {}, {}
+    for name in ("prefill_only", "long_prefill", "long_prefill_1024"):
+        if name not in W:
+            continue
+        w = W[name]
+        n = len(w["fns"]) * max(1, K // len(w["fns"])) if name == "prefill_only" else max(K, 2 * len(w["fns"]))
+        ms = timer.span_ms(w["fns"], n) / n
+        rooflines[name] = prefill_roofline(name, w, ms)
+    for name in ("short_decode", "long_beam"):
+        if name not in W:
+            continue
+        w, cfg = W[name], W[name]["cfg"]
+        R, Wb, NS = cfg["r"], cfg["w"], cfg["steps"]
+        n = max(K, 8)
+        dec_ms = [timer.span_ms(w["decode"][s], n) / n for s in range(NS)]
+        reo_ms = [timer.span_ms(w["reorder"][s], n) / n for s in range(NS)]
+        dec_b = [wl.decode_bytes(R, Wb, cfg["nq"], cfg["nkv"], cfg["lp"], s + 1, cfg["d"]) for s in range(NS)]
+        dec_f = [wl.decode_flops(R, Wb, cfg["nq"], cfg["lp"], s + 1, cfg["d"]) for s in range(NS)]
+        reo_b = [wl.reorder_bytes(R, Wb, s + 1, cfg["nkv"], cfg["d"]) for s in range(NS)]
+        gbs = sum(dec_b) / (sum(dec_ms) * 1e-3) / 1e9
+        r = roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_b)), float(np.mean(dec_ms)),
+                 measured_traffic(f"{name}/decode"))
+        r.update({"kernel": "shared_prefix_decode_kernel", "us_per_step": [round(t * 1e3, 2) for t in dec_ms],
+                  "mfma_tflops": round(sum(dec_f) / (sum(dec_ms) * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(sum(dec_f) / (sum(dec_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        rooflines[f"{name}/decode"] = r
+        gbs = sum(reo_b) / (sum(reo_ms) * 1e-3) / 1e9
+        r = roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(reo_b)), float(np.mean(reo_ms)),
+                 measured_traffic(f"{name}/reorder"))
+        r.update({"kernel": "suffix_reorder_kernel", "us_per_step": [round(t * 1e3, 2) for t in reo_ms]})
+        rooflines[f"{name}/reorder"] = r
+        if "topk" in w:
+            n = max(K, 2 * len(w["topk"]))
+            ms = timer.span_ms(w["topk"], n) / n
+            b = wl.topk_bytes(R, Wb, cfg["vocab"], Wb)
+            r = roof("hbm", b / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", b, ms, measured_traffic(f"{name}/topk"))
+            r.update({"kernel": "topk_stage1_kernel + topk_stage2_kernel"})
+            rooflines[f"{name}/topk"] = r
 
-    # The prefill layer's roofline follows from its arithmetic intensity: below the ridge
-    # (2500 TFLOP/s / 8000 GB/s = 312.5 FLOP/B) HBM bounds it, above it the matrix cores do.
-    pre_bytes = wl.prefill_bytes(lengths, pcfg["nq"], pcfg["nkv"], pcfg["d"])
-    pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
-    if pre_flops / pre_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        pre_roof = roof("packed_gqa_prefill", "hbm", pre_gbs, PEAK_HBM_GBS, "GB/s", pre_bytes, pre_ms)
+    headline = "long_prefill_1024" if "long_prefill_1024" in rooflines else next(iter(rooflines))
+    hr = rooflines[headline]
+    if "tflops" in hr:
+        value, unit = hr["tflops"], "TFLOP/s"
     else:
-        pre_roof = roof("packed_gqa_prefill", "mfma", pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre_flops, pre_ms)
-    pre_roof.update({"flop_per_byte": round(pre_flops / pre_bytes, 1), "tflops": round(pre_tflops, 2),
-                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "gbs": round(pre_gbs, 1),
-                     "hbm_frac": round(pre_gbs / PEAK_HBM_GBS, 4)})
-    rooflines = {
-        "packed_gqa_prefill": pre_roof,
-        "shared_prefix_decode": roof("shared_prefix_decode", "hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_bytes)),
-                                     float(np.mean(dec_ms))),
-        "beam_topk": roof("beam_topk", "hbm", top_gbs, PEAK_HBM_GBS, "GB/s", top_bytes, top_ms),
-        "suffix_reorder": roof("suffix_reorder", "hbm", reo_gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(reo_bytes)),
-                               float(np.mean(reo_ms))),
-    }
-    rooflines["shared_prefix_decode"]["mfma_tflops"] = round(dec_flops / (sum(dec_ms) * 1e-3) / 1e12, 2)
+        value, unit = hr["achieved"], hr["unit"]
 
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(cases[0], pre_flops, args.cpu_seconds)
+    cpu = cpus = None
+    if args.cpu_seconds > 0 and args.only is None:
+        cpus = cpu_baselines(W, args.cpu_seconds)
+        cpu = cpus.get("long_prefill_1024")
 
     rec = {
-        "metric": "attention TFLOPS & %bf16 MFMA peak (prefill); GB/s & %HBM peak (beam decode)",
-        "value": round(pre_tflops, 3),
-        "unit": "TFLOP/s",
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -294,145 +381,117 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, N(0,3) logits; no weights)",
         "config": {
-            "workload": "prefill_only x28 layers + long_beam 5-step beam search",
-            "prefill": {"sequences": len(lengths), "total_tokens": int(sum(lengths)), "max_len": max_len,
-                        "num_q_heads": pcfg["nq"], "num_kv_heads": pcfg["nkv"], "head_dim": pcfg["d"],
-                        "launches_per_step": layers},
-            "beam": {"requests": R, "beams": W, "prefix_len": LP, "decode_steps": NS, "num_q_heads": NQ,
-                     "num_kv_heads": NKV, "head_dim": D, "vocab": V, "k_local": 2 * W, "k_global": W},
-            "global_batch": len(lengths),
-            "seq_len": max_len,
+            "workload": ("one pass over every measured workload: Prefill-Only request (28 layers), long packed "
+                         "prefill (120 lognormal), long packed prefill 120 x 1024 (headline), short-prompt beam "
+                         "decode (4 steps), long-prompt beam search (5 steps)") if args.only is None else args.only,
+            "headline": headline,
+            "workloads": {n: workload_config(W[n]) for n in W},
+            "global_batch": 120 if args.only is None else None,
+            "seq_len": 1024 if args.only is None else None,
         },
-        "prefill_pct_bf16_peak": round(100 * pre_tflops / PEAK_BF16_TFLOPS, 2),
-        "decode_gbs": round(dec_gbs, 1),
-        "decode_pct_hbm_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
-        "decode_us_per_step": [round(t * 1e3, 2) for t in dec_ms],
-        "topk_gbs": round(top_gbs, 1),
-        "reorder_gbs": round(reo_gbs, 1),
-        "roofline": rooflines["packed_gqa_prefill"],
+        "roofline": hr,
         "rooflines": rooflines,
         "cpu_baseline": cpu,
+        "cpu_baselines": cpus,
     }
     print(json.dumps(rec), flush=True)
 
 
-def timed_launches(fn, n, warmup):
-    """Average duration (ms) of n back-to-back calls fn(i), measured with HIP events on the launching stream
-    behind a spin gate (so the host's launch overhead is not counted)."""
-    import torch
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(n):
-        fn(i)
-    torch.cuda.synchronize()
-    host = time.perf_counter() - t0
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    torch.cuda._sleep(1 << 20)
-    b.record(stream)
-    torch.cuda.synchronize()
-    gate = int((1 << 20) / max(a.elapsed_time(b), 1e-3) * max(3.0 * host * 1e3, 2.0))
-    torch.cuda._sleep(gate)
-    a.record(stream)
-    for i in range(n):
-        fn(i)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / n
+def workload_config(w):
+    cfg = dict(w["cfg"])
+    cfg.pop("seed", None)
+    if w["kind"] == "prefill":
+        cfg["total_tokens"] = int(sum(w["lengths"]))
+        cfg["max_len"] = int(max(w["lengths"]))
+        cfg["sequences"] = len(w["lengths"])
+        cfg.pop("lengths", None)
+    return cfg
 
 
-def only_config(args, dev):
-    """One configuration other than the step's, timed by itself (--only)."""
-    import torch
-
-    import attention_bga_packed_amd as bga
-    import workloads as wl
-
-    name, K, W0 = args.only, max(args.steps, 1), max(args.warmup, 1)
-    cfg = wl.CONFIGS[name]
-    rec = {"metric": "attention TFLOPS & %bf16 MFMA peak (prefill); GB/s & %HBM peak (beam decode)",
-           "n_gpus": 1, "steps": K, "warmup": W0, "higher_is_better": True, "dtype": "bf16",
-           "data": "synthetic (seeded N(0,1) Q/K/V)", "vs_baseline": None}
-    if cfg["kind"] == "prefill":
-        lengths = wl.prefill_lengths(cfg)
-        # input sets rotated between launches: together larger than the 256 MB Infinity Cache
-        nsets = 2 if name == "long_prefill_1024" else 3
-        cases = [wl.make_prefill_case(lengths, cfg["nq"], cfg["nkv"], cfg["d"], cfg["seed"] * 1000 + i, dev)
-                 for i in range(nsets)]
-        cu = torch.from_numpy(cases[0].cu_seqlens).to(dev)
-        out = torch.empty_like(cases[0].q)
-        lse = torch.empty(cases[0].q.shape[:2], dtype=torch.float32, device=dev)
-        ms = timed_launches(lambda i: bga.packed_gqa_prefill(cases[i % nsets].q, cases[i % nsets].k, cases[i % nsets].v,
-                                                             cu, max(lengths), out=out, lse=lse), K, W0)
-        flops = wl.prefill_flops(lengths, cfg["nq"], cfg["d"])
-        t = sum(lengths)
-        hbm = wl.prefill_bytes(lengths, cfg["nq"], cfg["nkv"], cfg["d"])
-        tf = flops / (ms * 1e-3) / 1e12
-        gbs = hbm / (ms * 1e-3) / 1e9
-        if flops / hbm < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-            roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_per_launch": hbm}
-        else:
-            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / PEAK_BF16_TFLOPS, 4), "algorithmic_per_launch": flops}
-        roof.update({"traffic": None, "avg_launch_us": round(ms * 1e3, 2), "flop_per_byte": round(flops / hbm, 1),
-                     "tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "gbs": round(gbs, 1),
-                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
-        rec.update({"value": round(tf, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
-                    "config": {"workload": name, "sequences": len(lengths), "total_tokens": t,
-                               "max_len": max(lengths), "num_q_heads": cfg["nq"], "num_kv_heads": cfg["nkv"],
-                               "head_dim": cfg["d"], "input_sets": nsets},
-                    "roofline": roof})
-        return rec
-    # decode: every suffix length of the configuration, several input sets rotated
-    nsets = 4
-    cases = [wl.make_decode_case(cfg["r"], cfg["w"], cfg["lp"], cfg["ls_cap"], cfg["nq"], cfg["nkv"], cfg["d"],
-                                 cfg["seed"] * 1000 + i, dev) for i in range(nsets)]
-    out = torch.empty_like(cases[0].q)
-    lse = torch.empty(cases[0].q.shape[:3], dtype=torch.float32, device=dev)
-    per, tot_b, tot_ms = [], 0, 0.0
-    for ls in range(1, cfg["steps"] + 1):
-        ms = timed_launches(lambda i: bga.shared_prefix_decode(cases[i % nsets].q, cases[i % nsets].prefix_k,
-                                                               cases[i % nsets].prefix_v, cases[i % nsets].suffix_k,
-                                                               cases[i % nsets].suffix_v, ls, out=out, lse=lse), K, W0)
-        b = wl.decode_bytes(cfg["r"], cfg["w"], cfg["nq"], cfg["nkv"], cfg["lp"], ls, cfg["d"])
-        per.append(round(ms * 1e3, 2))
-        tot_b += b
-        tot_ms += ms
-    gbs = tot_b / (tot_ms * 1e-3) / 1e9
-    rec.update({"value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(tot_ms / cfg["steps"], 4),
-                "decode_us_per_step": per,
-                "config": {"workload": name, "requests": cfg["r"], "beams": cfg["w"], "prefix_len": cfg["lp"],
-                           "decode_steps": cfg["steps"], "num_q_heads": cfg["nq"], "num_kv_heads": cfg["nkv"],
-                           "head_dim": cfg["d"], "input_sets": nsets},
-                "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                             "algorithmic_per_launch": tot_b // cfg["steps"],
-                             "avg_launch_us": round(tot_ms / cfg["steps"] * 1e3, 2)}})
-    return rec
+def median_of_3(fn):
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(sorted(ts)[1])
 
 
-def cpu_baseline(case, flops, seconds):
-    """The fp64 oracle on one Prefill-Only layer, repeated until ~`seconds` of CPU work."""
-    import oracle
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baselines(W, scale):
+    """The fp64 oracle (never tuned for speed) on bounded samples of the same inputs, on the host
+    cores: median of three runs each, in the units of the GPU figures."""
     import numpy as np
 
-    q, k, v = case.q.cpu(), case.k.cpu(), case.v.cpu()
-    cu = np.asarray(case.cu_seqlens)
+    import oracle
+    import workloads as wl
+
     threads = oracle.num_threads(0)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.packed_prefill(q, k, v, cu, nthreads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    return {"value": round(flops * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x one Prefill-Only layer (15 sequences, T={int(cu[-1])}, 16/8 heads, d 128) "
-                      f"in {el:.1f} s"}
+    model = cpu_model()
+    out = {}
+
+    def rec(value, unit, sample, secs):
+        return {"value": round(value, 6), "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
+                "seconds_median_of_3": round(secs, 3), "cpu_model": model}
+
+    for name in ("prefill_only", "long_prefill", "long_prefill_1024"):
+        if name not in W:
+            continue
+        w = W[name]
+        c, cfg = w["cases"][0], w["cfg"]
+        lengths = w["lengths"]
+        # bounded sample: the first sequences of the batch up to scale x the 120 x 1024 batch's work (at the
+        # default scale every prefill batch is timed whole; about 2 s per run of the 120 x 1024 batch)
+        budget = scale * wl.causal_pairs([1024] * 120)
+        n, pairs = 0, 0
+        while n < len(lengths) and pairs + wl.causal_pairs([lengths[n]]) <= max(budget, wl.causal_pairs(lengths[:1])):
+            pairs += wl.causal_pairs([lengths[n]])
+            n += 1
+        t = int(sum(lengths[:n]))
+        q, k, v = c.q[:t].cpu(), c.k[:t].cpu(), c.v[:t].cpu()
+        cu = wl.cu_seqlens_from_lengths(lengths[:n])
+        secs = median_of_3(lambda: oracle.packed_prefill(q, k, v, cu, nthreads=threads))
+        flops = wl.prefill_flops(lengths[:n], cfg["nq"], cfg["d"])
+        out[name] = rec(flops / secs / 1e12, "TFLOP/s", f"{n} of {len(lengths)} sequences (T={t}, "
+                        f"{cfg['nq']}/{cfg['nkv']} heads, d {cfg['d']}), {flops / 1e9:.1f} GFLOP", secs)
+    for name in ("short_decode", "long_beam"):
+        if name not in W:
+            continue
+        w, cfg = W[name], W[name]["cfg"]
+        c = w["sets"][0]
+        ls = cfg["steps"]
+        nr = max(1, min(cfg["r"], int(round(scale * cfg["r"]))))
+        host = [t[:nr].cpu() for t in (c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v)]
+        secs = median_of_3(lambda: oracle.shared_prefix_decode(*host, ls, nthreads=threads))
+        b = wl.decode_bytes(nr, cfg["w"], cfg["nq"], cfg["nkv"], cfg["lp"], ls, cfg["d"])
+        out[f"{name}/decode"] = rec(b / secs / 1e9, "GB/s", f"{nr} of {cfg['r']} requests at suffix length {ls}, "
+                                    f"{b / 1e6:.1f} MB algorithmic", secs)
+        par = w["parents"][ls - 1][:nr].cpu().numpy() if "parents" in w else \
+            wl.make_parents(nr, cfg["w"], cfg["w"], seed=1)
+        secs = median_of_3(lambda: oracle.suffix_reorder(host[3], host[4], par, ls))
+        b = wl.reorder_bytes(nr, cfg["w"], ls, cfg["nkv"], cfg["d"])
+        out[f"{name}/reorder"] = rec(b / secs / 1e9, "GB/s", f"{nr} of {cfg['r']} requests at suffix length {ls}",
+                                     secs)
+        if "topk" in w:
+            rows = max(8, min(2 * cfg["w"], int(round(scale * 2 * cfg["w"]))))
+            x = w["logits"][0].view(-1, cfg["vocab"])[:rows].unsqueeze(0).cpu()   # the first beam rows of the step
+            cum = np.zeros((1, rows), np.float32)
+            secs = median_of_3(lambda: oracle.beam_topk(x, cum, 2 * cfg["w"], min(cfg["w"], rows * 2 * cfg["w"]),
+                                                        nthreads=threads))
+            b = wl.topk_bytes(1, rows, cfg["vocab"], cfg["w"])
+            out[f"{name}/topk"] = rec(b / secs / 1e9, "GB/s", f"{rows} of {cfg['r'] * cfg['w']} beam rows over the "
+                                      f"full vocabulary, k_local {2 * cfg['w']}", secs)
+    return out
 
 
 if __name__ == "__main__":
