@@ -48,11 +48,15 @@ def lib():
         L.oracle_packed_prefill.argtypes = [P, P, P, P, i32, i32, i32, i32, f64, P, P, i32]
         L.oracle_shared_prefix_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
                                                   f64, P, P, i32]
+        L.oracle_shared_prefix_decode_packed.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                                         f64, P, P, i32]
+        L.oracle_last_token_gather.argtypes = [P, P, i32, ctypes.c_int64, P]
         L.oracle_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32]
         L.oracle_beam_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
         L.oracle_beam_topk_given_lse.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
         L.oracle_num_threads.argtypes = [i32]
-        for f in (L.oracle_packed_prefill, L.oracle_shared_prefix_decode, L.oracle_suffix_reorder,
+        for f in (L.oracle_packed_prefill, L.oracle_shared_prefix_decode, L.oracle_shared_prefix_decode_packed,
+                  L.oracle_last_token_gather, L.oracle_suffix_reorder,
                   L.oracle_beam_topk, L.oracle_beam_topk_given_lse, L.oracle_num_threads):
             f.restype = i32
         _lib = L
@@ -111,6 +115,40 @@ def shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, suffix_len, 
     if rc:
         raise ValueError(f"oracle_shared_prefix_decode rejected its arguments ({rc})")
     return out, lse
+
+
+def shared_prefix_decode_packed(q, prefix_k, prefix_v, prefix_cu, suffix_k, suffix_v, suffix_len, scale=None,
+                                nthreads: int = 0):
+    """fp64 (out [R,W,Nq,D], lse [R,W,Nq]) of shared-prefix decode where request r's prompt is rows
+    prefix_cu[r]..prefix_cu[r+1]-1 of the packed prompt K/V [T_p, Nkv, D]."""
+    q, pk, pv = _bits(q), _bits(prefix_k), _bits(prefix_v)
+    sk, sv = _bits(suffix_k), _bits(suffix_v)
+    cu = np.ascontiguousarray(prefix_cu, dtype=np.int32)
+    r, w, nq, d = q.shape
+    nkv = pk.shape[1]
+    ls_cap = sk.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((r, w, nq, d), np.float64)
+    lse = np.zeros((r, w, nq), np.float64)
+    rc = lib().oracle_shared_prefix_decode_packed(_p(q), _p(pk), _p(pv), _p(cu), _p(sk), _p(sv), r, w, suffix_len,
+                                                  ls_cap, nq, nkv, d, float(scale), _p(out), _p(lse), nthreads)
+    if rc:
+        raise ValueError(f"oracle_shared_prefix_decode_packed rejected its arguments ({rc})")
+    return out, lse
+
+
+def last_token_gather(src: np.ndarray, cu_seqlens) -> np.ndarray:
+    """Row cu[i+1]-1 of src ([T, ...], any dtype) for every sequence i; zeros for empty sequences."""
+    src = np.ascontiguousarray(src)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    b = len(cu) - 1
+    row_bytes = src[0].nbytes if src.shape[0] else int(np.prod(src.shape[1:])) * src.itemsize
+    dst = np.empty((b,) + src.shape[1:], src.dtype)
+    rc = lib().oracle_last_token_gather(_p(src), _p(cu), b, row_bytes, _p(dst))
+    if rc:
+        raise ValueError(f"oracle_last_token_gather rejected its arguments ({rc})")
+    return dst
 
 
 def suffix_reorder(src_k, src_v, parent, suffix_len, src_tokens=None, num_tokens=0):

@@ -169,6 +169,83 @@ int32_t oracle_shared_prefix_decode(const uint16_t *q, const uint16_t *pk, const
 }
 
 /*
+ * Shared-prefix beam decode where every request has a prompt of its own length,
+ * the prompt K/V kept packed exactly as the packed prefill leaves it (article
+ * section 3.2 equation; the packed layout of section 3.1). Request r's prompt is
+ * rows prefix_cu[r] .. prefix_cu[r+1]-1 of pk/pv [T_p, nkv, d]; q, suffix, out
+ * and lse as in oracle_shared_prefix_decode. The concatenation
+ * [prompt of r; suffix of (r, b)] is again built explicitly.
+ */
+int32_t oracle_shared_prefix_decode_packed(const uint16_t *q, const uint16_t *pk, const uint16_t *pv,
+                                           const int32_t *prefix_cu, const uint16_t *sk, const uint16_t *sv,
+                                           int32_t R, int32_t W, int32_t Ls, int32_t Ls_cap, int32_t nq,
+                                           int32_t nkv, int32_t d, double scale, double *out, double *lse,
+                                           int32_t nthreads)
+{
+    if (!q || !prefix_cu || !out || !lse) return 1;
+    if (Ls > 0 && (!sk || !sv)) return 1;
+    if (R < 0 || W < 0 || Ls < 0 || Ls > Ls_cap || nq <= 0 || nkv <= 0 || nq % nkv || d <= 0) return 2;
+    for (int32_t r = 0; r < R; ++r) {
+        const int64_t lp = (int64_t)prefix_cu[r + 1] - prefix_cu[r];
+        if (lp < 0 || lp + Ls == 0) return 2;
+        if (lp > 0 && (!pk || !pv)) return 1;
+    }
+    const int32_t group = nq / nkv;
+    const int64_t units = (int64_t)R * W * nkv;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(pick_threads(nthreads))
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int64_t r = unit / ((int64_t)W * nkv), b = (unit / nkv) % W, g = unit % nkv;
+        const int64_t p0 = prefix_cu[r], lp = (int64_t)prefix_cu[r + 1] - p0, n = lp + Ls;
+        double *kc = malloc(sizeof(double) * n * d), *vc = malloc(sizeof(double) * n * d);
+        double *qq = malloc(sizeof(double) * d), *s = malloc(sizeof(double) * n), *o = malloc(sizeof(double) * d);
+        for (int64_t u = 0; u < lp; ++u)
+            for (int32_t e = 0; e < d; ++e) {
+                kc[u * d + e] = widen(pk[((p0 + u) * nkv + g) * d + e]);
+                vc[u * d + e] = widen(pv[((p0 + u) * nkv + g) * d + e]);
+            }
+        for (int64_t j = 0; j < Ls; ++j)
+            for (int32_t e = 0; e < d; ++e) {
+                const int64_t at = (((r * W + b) * Ls_cap + j) * nkv + g) * d + e;
+                kc[(lp + j) * d + e] = widen(sk[at]);
+                vc[(lp + j) * d + e] = widen(sv[at]);
+            }
+        for (int32_t hg = 0; hg < group; ++hg) {
+            const int64_t row = (r * W + b) * nq + g * group + hg;
+            for (int32_t e = 0; e < d; ++e) qq[e] = widen(q[row * d + e]);
+            attend(qq, kc, vc, n, d, scale, s, o, &lse[row]);
+            for (int32_t e = 0; e < d; ++e) out[row * d + e] = o[e];
+        }
+        free(kc); free(vc); free(qq); free(s); free(o);
+    }
+    return 0;
+}
+
+/*
+ * The last valid token of every packed sequence (article section 3.1: after
+ * packed attention the same sequence boundary selects each sequence's
+ * last-position hidden state). Row i of dst is row cu[i+1]-1 of src (rows of
+ * row_bytes bytes); a zero-length sequence has no last token and gets a row of
+ * zeros. Pure copy.
+ */
+int32_t oracle_last_token_gather(const uint8_t *src, const int32_t *cu, int32_t num_seqs, int64_t row_bytes,
+                                 uint8_t *dst)
+{
+    if (!cu || !dst || (num_seqs > 0 && !src)) return 1;
+    if (num_seqs < 0 || row_bytes < 0) return 2;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const int64_t len = (int64_t)cu[i + 1] - cu[i];
+        if (len < 0) return 2;
+        if (len == 0) {
+            memset(dst + (int64_t)i * row_bytes, 0, (size_t)row_bytes);
+            continue;
+        }
+        const int64_t last = (int64_t)cu[i + 1] - 1;
+        memcpy(dst + (int64_t)i * row_bytes, src + last * row_bytes, (size_t)row_bytes);
+    }
+    return 0;
+}
+
+/*
  * Parent-index reorder (article sections 3.2 and 3.3): new beam b takes the
  * suffix K/V (first Ls positions) and the token history of beam parent[r, b].
  * The prompt K/V is not touched. Pure copy.

@@ -43,6 +43,15 @@ MUTANTS = [
      "const int64_t row = (r * W + b) * nq + hg * nkv + g;"),
     ("prompt of request 0", "kc[u * d + e] = widen(pk[((r * Lp + u) * nkv + g) * d + e]);",
      "kc[u * d + e] = widen(pk[((0 * Lp + u) * nkv + g) * d + e]);"),
+    # shared-prefix decode over packed prompts of their own lengths
+    ("packed prompt start ignored", "kc[u * d + e] = widen(pk[((p0 + u) * nkv + g) * d + e]);",
+     "kc[u * d + e] = widen(pk[((u) * nkv + g) * d + e]);"),
+    ("packed suffix over the prompt", "kc[(lp + j) * d + e] = widen(sk[at]);", "kc[(j) * d + e] = widen(sk[at]);"),
+    # last-token gather
+    ("first token instead of last", "const int64_t last = (int64_t)cu[i + 1] - 1;",
+     "const int64_t last = (int64_t)cu[i];"),
+    ("empty sequence not zeroed", "memset(dst + (int64_t)i * row_bytes, 0, (size_t)row_bytes);",
+     "memset(dst + (int64_t)i * row_bytes, 1, (size_t)row_bytes);"),
     # suffix reorder
     ("reorder scatters", "dst_k[((r * W + b) * Ls_cap + j) * row + e] = src_k[((r * W + p) * Ls_cap + j) * row + e];",
      "dst_k[((r * W + p) * Ls_cap + j) * row + e] = src_k[((r * W + b) * Ls_cap + j) * row + e];"),

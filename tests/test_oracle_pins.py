@@ -197,6 +197,59 @@ def test_decode_beam_permutation_equivariance():
     assert np.array_equal(o2, o[:, perm.numpy()]) and np.array_equal(l2, lse[:, perm.numpy()])
 
 
+def packed_prompt_case(lps=(7, 0, 3), w=5, ls_cap=3, nq=4, nkv=2, d=64, seed=23):
+    """Prompts of different lengths packed back to back [sum Lp, Nkv, D], plus per-beam suffixes."""
+    c = wl.make_decode_case(len(lps), w, 1, ls_cap, nq, nkv, d, seed)
+    gen = torch.Generator().manual_seed(seed + 1)
+    tp = int(sum(lps))
+    pk = wl.bf16_normal((tp, nkv, d), gen, "cpu")
+    pv = wl.bf16_normal((tp, nkv, d), gen, "cpu")
+    return c, pk, pv, wl.cu_seqlens_from_lengths(lps)
+
+
+@pytest.mark.parametrize("lps,ls,w", [((7, 0, 3), 2, 5), ((1, 9), 0, 3), ((4, 4, 4), 1, 1), ((0, 2), 3, 2)])
+def test_decode_packed_prompts_match_sdpa_over_concat(lps, ls, w):
+    """Prompts of their own lengths (0 included when the suffix is not empty), kept packed: SDPA (float64)
+    over the explicit [prompt of r; suffix of beam b] of every beam; W = 1 is ordinary decode."""
+    c, pk, pv, cu = packed_prompt_case(lps, w)
+    scale = 1.0 / np.sqrt(c.d)
+    o, lse = oracle.shared_prefix_decode_packed(c.q, pk, pv, cu, c.suffix_k, c.suffix_v, ls, scale)
+    g = c.nq // c.nkv
+    for r in range(c.r):
+        for b in range(c.w):
+            kc = torch.cat([pk[cu[r]:cu[r + 1]], c.suffix_k[r, b, :ls]]).double()
+            vc = torch.cat([pv[cu[r]:cu[r + 1]], c.suffix_v[r, b, :ls]]).double()
+            kc = kc.repeat_interleave(g, dim=1).transpose(0, 1)
+            vc = vc.repeat_interleave(g, dim=1).transpose(0, 1)
+            q = c.q[r, b].double()[:, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(q, kc, vc, scale=scale)[:, 0]
+            assert np.max(np.abs(o[r, b] - ref.numpy())) < 1e-12
+            sc = scale * (q @ kc.transpose(1, 2))[:, 0].numpy()
+            assert np.max(np.abs(lse[r, b] - logsumexp(sc, axis=-1))) < 1e-12
+
+
+def test_decode_packed_prompt_rejects_a_beam_without_keys():
+    c, pk, pv, cu = packed_prompt_case((3, 0), 2)
+    with pytest.raises(ValueError):
+        oracle.shared_prefix_decode_packed(c.q, pk, pv, cu, c.suffix_k, c.suffix_v, 0)
+
+
+def test_last_token_gather_matches_fancy_indexing():
+    lengths = [3, 0, 1, 7, 0, 2]
+    cu = wl.cu_seqlens_from_lengths(lengths)
+    x = np.random.default_rng(4).integers(0, 1 << 16, (int(cu[-1]), 5, 6)).astype(np.uint16)
+    y = oracle.last_token_gather(x, cu)
+    for i, n in enumerate(lengths):
+        if n:
+            assert np.array_equal(y[i], x[cu[i + 1] - 1])
+        else:
+            assert not y[i].any()
+    # every sequence of one token: the gather is the identity
+    ones = wl.cu_seqlens_from_lengths([1] * 6)
+    z = np.arange(6 * 8, dtype=np.float32).reshape(6, 8)
+    assert np.array_equal(oracle.last_token_gather(z, ones), z)
+
+
 # ------------------------------------------------------------- C-3 reorder
 
 def test_reorder_identity_and_gather():
