@@ -15,9 +15,11 @@ from ._binding import (  # noqa: F401
     beam_topk,
     beam_topk_noalloc,
     beam_topk_workspace_size,
+    last_token_gather,
     lib,
     load_library,
     packed_gqa_prefill,
     shared_prefix_decode,
+    shared_prefix_decode_packed,
     suffix_reorder,
 )

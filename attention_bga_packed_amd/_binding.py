@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "BGA_OK", 1: "BGA_ERR_NULL", 2: "BGA_ERR_SHAPE", 3: "BGA_ERR_
 # Every symbol declared in include/bga.h.
 EXPORTS = ("bga_packed_gqa_prefill", "bga_shared_prefix_decode", "bga_suffix_reorder",
            "bga_beam_topk_workspace_size", "bga_beam_topk", "bga_status_string", "bga_last_hip_error",
-           "bga_version", "bga_debug_build", "bga_last_violations", "bga_beam_topk_noalloc")
+           "bga_version", "bga_debug_build", "bga_last_violations", "bga_beam_topk_noalloc",
+           "bga_shared_prefix_decode_packed", "bga_last_token_gather")
 
 
 class BgaError(RuntimeError):
@@ -47,6 +48,9 @@ def load_library(path: str = LIB_PATH):
     P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     L.bga_packed_gqa_prefill.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, P, P, P]
     L.bga_shared_prefix_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P, P]
+    L.bga_shared_prefix_decode_packed.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32, f32, P,
+                                                  P, P]
+    L.bga_last_token_gather.argtypes = [P, P, i32, i32, ctypes.c_int64, P, P]
     L.bga_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, P]
     L.bga_beam_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.bga_beam_topk_workspace_size.restype = sz
@@ -59,7 +63,8 @@ def load_library(path: str = LIB_PATH):
     L.bga_debug_build.argtypes = []
     L.bga_last_violations.argtypes = []
     L.bga_last_violations.restype = ctypes.c_uint32
-    for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_suffix_reorder, L.bga_beam_topk,
+    for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_shared_prefix_decode_packed,
+              L.bga_last_token_gather, L.bga_suffix_reorder, L.bga_beam_topk,
               L.bga_beam_topk_noalloc, L.bga_last_hip_error, L.bga_version, L.bga_debug_build):
         f.restype = i32
     return L
@@ -163,6 +168,58 @@ def shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, suffix_len: 
                                       _ptr(lse), _stream(q))
     _check(st, "bga_shared_prefix_decode")
     return out, lse
+
+
+def shared_prefix_decode_packed(q, prefix_k, prefix_v, prefix_cu, suffix_k, suffix_v, suffix_len: int,
+                                softmax_scale=None, out=None, lse=None, want_lse: bool = True):
+    """Shared-prefix beam decode over prompts of their own lengths kept packed: q [R,W,Nq,D]; prefix [T_p,Nkv,D]
+    with request r's prompt at rows prefix_cu[r]..prefix_cu[r+1]-1 (prefix_cu int32 [R+1] on the GPU);
+    suffix [R,W,Ls_cap,Nkv,D] (bf16). Returns (out [R,W,Nq,D] bf16, lse [R,W,Nq] fp32 or None)."""
+    _need(q, "q", torch.bfloat16, ndim=4)
+    dev = q.device
+    r, w, nq, d = q.shape
+    _need(prefix_k, "prefix_k", torch.bfloat16, dev, 3)
+    tp, nkv = prefix_k.shape[0], prefix_k.shape[1]
+    if prefix_k.shape[2] != d:
+        raise ValueError("prefix K/V must be [T_p, Nkv, D]")
+    _need(prefix_v, "prefix_v", torch.bfloat16, dev, shape=prefix_k.shape)
+    _need(prefix_cu, "prefix_cu", torch.int32, dev, shape=(r + 1,))
+    _need(suffix_k, "suffix_k", torch.bfloat16, dev, 5)
+    ls_cap = suffix_k.shape[2]
+    if suffix_k.shape != (r, w, ls_cap, nkv, d):
+        raise ValueError("suffix K/V must be [R, W, Ls_cap, Nkv, D]")
+    _need(suffix_v, "suffix_v", torch.bfloat16, dev, shape=suffix_k.shape)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev, shape=q.shape)
+    if lse is None and want_lse:
+        lse = torch.empty((r, w, nq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, shape=(r, w, nq))
+    st = lib.bga_shared_prefix_decode_packed(_ptr(q), _ptr(prefix_k), _ptr(prefix_v), _ptr(prefix_cu), tp,
+                                             _ptr(suffix_k), _ptr(suffix_v), r, w, int(suffix_len), ls_cap, nq, nkv,
+                                             d, float(softmax_scale), _ptr(out), _ptr(lse), _stream(q))
+    _check(st, "bga_shared_prefix_decode_packed")
+    return out, lse
+
+
+def last_token_gather(src, cu_seqlens, out=None):
+    """Row cu[i+1]-1 of src [T, ...] for every sequence i (zeros for an empty one) -> [B, ...]."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous() or src.dim() < 1:
+        raise ValueError("src must be a contiguous GPU tensor [T, ...]")
+    dev = src.device
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+    b = cu_seqlens.numel() - 1
+    row_bytes = src.element_size() * (src[0].numel() if src.shape[0] else int(math.prod(src.shape[1:])))
+    if out is None:
+        out = torch.empty((b,) + tuple(src.shape[1:]), dtype=src.dtype, device=dev)
+    _need(out, "out", src.dtype, dev, shape=(b,) + tuple(src.shape[1:]))
+    st = lib.bga_last_token_gather(_ptr(src), _ptr(cu_seqlens), b, src.shape[0], int(row_bytes), _ptr(out),
+                                   _stream(src))
+    _check(st, "bga_last_token_gather")
+    return out
 
 
 def suffix_reorder(src_k, src_v, parent, suffix_len: int, dst_k=None, dst_v=None, src_tokens=None,

@@ -86,6 +86,35 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
                                                  num_kv_heads, head_dim, softmax_scale, out, lse, stream));
 }
 
+// Host checks shared by both decode entry points (prompt-specific checks are the caller's).
+static bga_status decode_check(const bga_bf16 *q, const bga_bf16 *suffix_k, const bga_bf16 *suffix_v,
+                               int32_t num_requests, int32_t beam_width, int32_t suffix_len, int32_t suffix_cap,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                               const bga_bf16 *out, const float *lse)
+{
+    if (num_requests < 0 || beam_width < 0 || suffix_len < 0 || suffix_cap < 0) return BGA_ERR_SHAPE;
+    if (suffix_len > suffix_cap) return BGA_ERR_SHAPE;
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return BGA_ERR_SHAPE;
+    if (!heads_ok(num_q_heads, num_kv_heads)) return BGA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
+    if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * num_kv_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * beam_width * num_q_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // output row index
+    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
+    if (num_requests == 0 || beam_width == 0) return BGA_OK;
+    if (!q || !out) return BGA_ERR_NULL;
+    if (suffix_len > 0 && (!suffix_k || !suffix_v)) return BGA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(suffix_k, 16) || !aligned(suffix_v, 16) ||
+        (lse && !aligned(lse, 4)))
+        return BGA_ERR_ALIGN;
+    const size_t obytes = (size_t)num_requests * beam_width * num_q_heads * head_dim * 2;
+    const size_t sbytes = (size_t)num_requests * beam_width * suffix_cap * num_kv_heads * head_dim * 2;
+    if (overlap(out, obytes, q, obytes) || overlap(out, obytes, suffix_k, sbytes) ||
+        overlap(out, obytes, suffix_v, sbytes))
+        return BGA_ERR_ALIAS;
+    return BGA_OK;
+}
+
 bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k, const bga_bf16 *prefix_v,
                                     const bga_bf16 *suffix_k, const bga_bf16 *suffix_v, int32_t num_requests,
                                     int32_t beam_width, int32_t prefix_len, int32_t suffix_len,
@@ -93,35 +122,78 @@ bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k,
                                     int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
                                     hipStream_t stream)
 {
-    if (num_requests < 0 || beam_width < 0 || prefix_len < 0 || suffix_len < 0 || suffix_cap < 0)
-        return BGA_ERR_SHAPE;
-    if (suffix_len > suffix_cap || prefix_len + suffix_len < 1) return BGA_ERR_SHAPE;
-    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return BGA_ERR_SHAPE;
-    if (!heads_ok(num_q_heads, num_kv_heads)) return BGA_ERR_UNSUPPORTED;
-    if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
-    if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX || prefix_len > BGA_MAX_SEQLEN)
-        return BGA_ERR_UNSUPPORTED;
-    if ((int64_t)num_requests * num_kv_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
-    if ((int64_t)num_requests * beam_width * num_q_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // output row index
-    if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
-    if (num_requests == 0 || beam_width == 0) return BGA_OK;
-    if (!q || !out) return BGA_ERR_NULL;
+    if (prefix_len < 0) return BGA_ERR_SHAPE;
+    if (prefix_len + (int64_t)suffix_len < 1) return BGA_ERR_SHAPE;
+    bga_status st = decode_check(q, suffix_k, suffix_v, num_requests, beam_width, suffix_len, suffix_cap, num_q_heads,
+                                 num_kv_heads, head_dim, softmax_scale, out, lse);
+    if (st == BGA_OK && prefix_len > BGA_MAX_SEQLEN) st = BGA_ERR_UNSUPPORTED;
+    if (st != BGA_OK || num_requests == 0 || beam_width == 0) return st;
     if (prefix_len > 0 && (!prefix_k || !prefix_v)) return BGA_ERR_NULL;
-    if (suffix_len > 0 && (!suffix_k || !suffix_v)) return BGA_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(prefix_k, 16) || !aligned(prefix_v, 16) ||
-        !aligned(suffix_k, 16) || !aligned(suffix_v, 16) || (lse && !aligned(lse, 4)))
-        return BGA_ERR_ALIGN;
+    if (!aligned(prefix_k, 16) || !aligned(prefix_v, 16)) return BGA_ERR_ALIGN;
     const size_t obytes = (size_t)num_requests * beam_width * num_q_heads * head_dim * 2;
     const size_t pbytes = (size_t)num_requests * prefix_len * num_kv_heads * head_dim * 2;
-    const size_t sbytes = (size_t)num_requests * beam_width * suffix_cap * num_kv_heads * head_dim * 2;
-    if (overlap(out, obytes, q, obytes) || overlap(out, obytes, prefix_k, pbytes) ||
-        overlap(out, obytes, prefix_v, pbytes) || overlap(out, obytes, suffix_k, sbytes) ||
-        overlap(out, obytes, suffix_v, sbytes))
+    if (overlap(out, obytes, prefix_k, pbytes) || overlap(out, obytes, prefix_v, pbytes)) return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_shared_prefix_decode(q, prefix_k, prefix_v, nullptr, suffix_k, suffix_v,
+                                                       num_requests, beam_width, prefix_len, suffix_len, suffix_cap,
+                                                       num_q_heads, num_kv_heads, head_dim, softmax_scale, out, lse,
+                                                       stream));
+}
+
+bga_status bga_shared_prefix_decode_packed(const bga_bf16 *q, const bga_bf16 *prefix_k, const bga_bf16 *prefix_v,
+                                           const int32_t *prefix_cu, int32_t total_prefix_tokens,
+                                           const bga_bf16 *suffix_k, const bga_bf16 *suffix_v,
+                                           int32_t num_requests, int32_t beam_width, int32_t suffix_len,
+                                           int32_t suffix_cap, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
+                                           hipStream_t stream)
+{
+    if (total_prefix_tokens < 0) return BGA_ERR_SHAPE;
+    if (total_prefix_tokens == 0 && suffix_len == 0 && num_requests > 0) return BGA_ERR_SHAPE;   // no key anywhere
+    bga_status st = decode_check(q, suffix_k, suffix_v, num_requests, beam_width, suffix_len, suffix_cap, num_q_heads,
+                                 num_kv_heads, head_dim, softmax_scale, out, lse);
+    if (st != BGA_OK || num_requests == 0 || beam_width == 0) return st;
+    if (!prefix_cu) return BGA_ERR_NULL;
+    if (total_prefix_tokens > 0 && (!prefix_k || !prefix_v)) return BGA_ERR_NULL;
+    if (!aligned(prefix_k, 16) || !aligned(prefix_v, 16) || !aligned(prefix_cu, 4)) return BGA_ERR_ALIGN;
+    const size_t obytes = (size_t)num_requests * beam_width * num_q_heads * head_dim * 2;
+    const size_t pbytes = (size_t)total_prefix_tokens * num_kv_heads * head_dim * 2;
+    if (overlap(out, obytes, prefix_k, pbytes) || overlap(out, obytes, prefix_v, pbytes)) return BGA_ERR_ALIAS;
+#ifdef BGA_DEBUG
+    {
+        uint32_t bad = 0;
+        st = check_status(bga::debug_check_prompts(prefix_cu, num_requests, total_prefix_tokens, BGA_MAX_SEQLEN,
+                                                   suffix_len == 0, stream, &bad),
+                          bad);
+        if (st != BGA_OK) return st;
+    }
+#endif
+    return hip_status(bga::launch_shared_prefix_decode(q, prefix_k, prefix_v, prefix_cu, suffix_k, suffix_v,
+                                                       num_requests, beam_width, 0, suffix_len, suffix_cap,
+                                                       num_q_heads, num_kv_heads, head_dim, softmax_scale, out, lse,
+                                                       stream));
+}
+
+bga_status bga_last_token_gather(const void *src, const int32_t *cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int64_t row_bytes, void *dst, hipStream_t stream)
+{
+    if (num_seqs < 0 || total_tokens < 0 || row_bytes <= 0 || row_bytes % 16) return BGA_ERR_SHAPE;
+    if (num_seqs > 0x7fffffff / 2 || row_bytes / 16 > ((int64_t)1 << 40)) return BGA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return BGA_OK;
+    if (!cu_seqlens || !dst || (total_tokens > 0 && !src)) return BGA_ERR_NULL;
+    if (!aligned(dst, 16) || (src && !aligned(src, 16)) || !aligned(cu_seqlens, 4)) return BGA_ERR_ALIGN;
+    if (total_tokens > 0 && overlap(dst, (size_t)num_seqs * row_bytes, src, (size_t)total_tokens * row_bytes))
         return BGA_ERR_ALIAS;
-    return hip_status(bga::launch_shared_prefix_decode(q, prefix_k, prefix_v, suffix_k, suffix_v, num_requests,
-                                                       beam_width, prefix_len, suffix_len, suffix_cap,
-                                                       num_q_heads, num_kv_heads, head_dim, softmax_scale, out,
-                                                       lse, stream));
+#ifdef BGA_DEBUG
+    {
+        uint32_t bad = 0;
+        const bga_status st =
+            check_status(bga::debug_check_prompts(cu_seqlens, num_seqs, total_tokens, 0x7fffffff, false, stream, &bad),
+                         bad);
+        if (st != BGA_OK) return st;
+    }
+#endif
+    return hip_status(bga::launch_last_token_gather(total_tokens > 0 ? src : dst, cu_seqlens, num_seqs,
+                                                    total_tokens > 0 ? total_tokens : 1, row_bytes, dst, stream));
 }
 
 bga_status bga_suffix_reorder(const bga_bf16 *src_k, const bga_bf16 *src_v, bga_bf16 *dst_k, bga_bf16 *dst_v,

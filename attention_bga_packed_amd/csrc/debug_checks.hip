@@ -30,13 +30,14 @@ __device__ __forceinline__ void flag(bool bad, uint32_t bit)
 
 __global__ void clear_word_kernel(uint32_t *w) { *w = 0u; }
 
-// cu[0] == 0, cu non-decreasing, cu[B] == T, every length <= max_seqlen
+// cu[0] == 0, cu non-decreasing, cu[B] == T, every length <= max_seqlen (and
+// >= 1 when need_nonempty)
 __global__ __launch_bounds__(256) void check_cu_seqlens_kernel(const int32_t *__restrict__ cu, int B, int T,
-                                                               int max_seqlen)
+                                                               int max_seqlen, bool need_nonempty)
 {
     for (int i0 = blockIdx.x * 256; i0 <= B; i0 += gridDim.x * 256) {
         const int i = i0 + (int)threadIdx.x;
-        bool bad_cu = false, bad_len = false;
+        bool bad_cu = false, bad_len = false, empty = false;
         if (i <= B) {
             const int c = cu[i];
             if (i == 0) bad_cu |= c != 0;
@@ -45,10 +46,12 @@ __global__ __launch_bounds__(256) void check_cu_seqlens_kernel(const int32_t *__
                 const int n = cu[i + 1] - c;
                 bad_cu |= n < 0;
                 bad_len |= n > max_seqlen;
+                empty = need_nonempty && n == 0;
             }
         }
         flag(bad_cu, BGA_VIOLATION_CU_SEQLENS);
         flag(bad_len, BGA_VIOLATION_MAX_SEQLEN);
+        flag(empty, BGA_VIOLATION_NO_KEYS);
     }
 }
 
@@ -120,7 +123,16 @@ hipError_t debug_check_prefill(const int32_t *cu, int B, int T, int max_seqlen, 
 {
     return run_check(stream, violations, [&] {
         hipLaunchKernelGGL(check_cu_seqlens_kernel, dim3(grid_for((size_t)B + 1)), dim3(256), 0, stream, cu, B, T,
-                           max_seqlen);
+                           max_seqlen, false);
+    });
+}
+
+hipError_t debug_check_prompts(const int32_t *cu, int R, int T, int max_len, bool need_nonempty, hipStream_t stream,
+                               uint32_t *violations)
+{
+    return run_check(stream, violations, [&] {
+        hipLaunchKernelGGL(check_cu_seqlens_kernel, dim3(grid_for((size_t)R + 1)), dim3(256), 0, stream, cu, R, T,
+                           max_len, need_nonempty);
     });
 }
 

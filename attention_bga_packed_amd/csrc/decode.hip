@@ -21,6 +21,11 @@
 // Grid = (R*Nkv, row blocks). Consecutive workgroups are dealt round-robin over
 // the 8 XCDs, so with R*Nkv a multiple of 8 every row block of one
 // (request, kv head) lands on the same XCD and shares its L2 copy of the prefix.
+//
+// Prompt layout. Either every request has a prompt of Lp tokens at
+// [R, Lp, Nkv, D], or (prefix_cu given) the prompts are packed back to back,
+// exactly as the packed prefill leaves its K/V: request r's prompt is rows
+// prefix_cu[r] .. prefix_cu[r+1]-1 of [T_p, Nkv, D], each of its own length.
 #include "attn_core.hpp"
 #include "internal.hpp"
 
@@ -31,8 +36,9 @@ using namespace core;
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void shared_prefix_decode_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ pk, const uint16_t *__restrict__ pv,
-    const uint16_t *__restrict__ sk, const uint16_t *__restrict__ sv, int W, int Lp, int Ls, int Ls_cap, int nq,
-    int nkv, int group, float scale, uint16_t *__restrict__ out, float *__restrict__ lse)
+    const int32_t *__restrict__ pcu, const uint16_t *__restrict__ sk, const uint16_t *__restrict__ sv, int W,
+    int Lp_uniform, int Ls, int Ls_cap, int nq, int nkv, int group, float scale, uint16_t *__restrict__ out,
+    float *__restrict__ lse)
 {
     using G = Geo<D>;
     constexpr int NW = 4;
@@ -54,7 +60,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
     const uint32_t lds_base = (uint32_t)(size_t)(const BGA_LDS char *)smem;
     const uint32_t rbytes = (uint32_t)(nkv * D * 2);
-    const size_t pofs = ((size_t)r * Lp * nkv + g) * D;
+    // this request's prompt: rows p0 .. p0 + Lp - 1 (wave-uniform scalar loads)
+    const int p0 = pcu ? uni(pcu[r]) : r * Lp_uniform;
+    const int Lp = pcu ? uni(pcu[r + 1]) - p0 : Lp_uniform;
+    const size_t pofs = ((size_t)p0 * nkv + g) * D;
     const uint64_t kbase = uni64((uint64_t)(size_t)(pk + pofs));
     const uint64_t vbase = uni64((uint64_t)(size_t)(pv + pofs));
     const int nkt = (Lp + G::BN - 1) / G::BN;
@@ -186,9 +195,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 }
 
 template <int D>
-static hipError_t launch_decode_d(const uint16_t *q, const uint16_t *pk, const uint16_t *pv, const uint16_t *sk,
-                                  const uint16_t *sv, int R, int W, int Lp, int Ls, int Ls_cap, int nq, int nkv,
-                                  float scale, uint16_t *out, float *lse, hipStream_t stream)
+static hipError_t launch_decode_d(const uint16_t *q, const uint16_t *pk, const uint16_t *pv, const int32_t *pcu,
+                                  const uint16_t *sk, const uint16_t *sv, int R, int W, int Lp, int Ls, int Ls_cap,
+                                  int nq, int nkv, float scale, uint16_t *out, float *lse, hipStream_t stream)
 {
     const int group = nq / nkv;
     const int rows = W * group;
@@ -197,19 +206,21 @@ static hipError_t launch_decode_d(const uint16_t *q, const uint16_t *pk, const u
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     dim3 grid(R * nkv, (rows + 127) / 128), block(256);
-    hipLaunchKernelGGL(shared_prefix_decode_kernel<D>, grid, block, smem, stream, q, pk, pv, sk, sv, W, Lp, Ls,
-                       Ls_cap, nq, nkv, group, scale, out, lse);
+    hipLaunchKernelGGL(shared_prefix_decode_kernel<D>, grid, block, smem, stream, q, pk, pv, pcu, sk, sv, W, Lp,
+                       Ls, Ls_cap, nq, nkv, group, scale, out, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_shared_prefix_decode(const uint16_t *q, const uint16_t *pk, const uint16_t *pv,
-                                       const uint16_t *sk, const uint16_t *sv, int R, int W, int Lp, int Ls,
-                                       int Ls_cap, int nq, int nkv, int d, float scale, uint16_t *out, float *lse,
-                                       hipStream_t stream)
+                                       const int32_t *prefix_cu, const uint16_t *sk, const uint16_t *sv, int R,
+                                       int W, int Lp, int Ls, int Ls_cap, int nq, int nkv, int d, float scale,
+                                       uint16_t *out, float *lse, hipStream_t stream)
 {
     if (d == 64)
-        return launch_decode_d<64>(q, pk, pv, sk, sv, R, W, Lp, Ls, Ls_cap, nq, nkv, scale, out, lse, stream);
-    return launch_decode_d<128>(q, pk, pv, sk, sv, R, W, Lp, Ls, Ls_cap, nq, nkv, scale, out, lse, stream);
+        return launch_decode_d<64>(q, pk, pv, prefix_cu, sk, sv, R, W, Lp, Ls, Ls_cap, nq, nkv, scale, out, lse,
+                                   stream);
+    return launch_decode_d<128>(q, pk, pv, prefix_cu, sk, sv, R, W, Lp, Ls, Ls_cap, nq, nkv, scale, out, lse,
+                                stream);
 }
 
 }  // namespace bga

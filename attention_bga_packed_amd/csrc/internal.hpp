@@ -14,10 +14,15 @@ hipError_t launch_packed_prefill(const uint16_t *q, const uint16_t *k, const uin
                                  int num_seqs, int max_seqlen, int nq, int nkv, int d, float scale, uint16_t *out,
                                  float *lse, hipStream_t stream);
 
+// prefix_cu == nullptr: prompts of Lp tokens at [R, Lp, Nkv, D]; else request r's
+// prompt is rows prefix_cu[r] .. prefix_cu[r+1]-1 of a packed [T_p, Nkv, D].
 hipError_t launch_shared_prefix_decode(const uint16_t *q, const uint16_t *pk, const uint16_t *pv,
-                                       const uint16_t *sk, const uint16_t *sv, int R, int W, int Lp, int Ls,
-                                       int Ls_cap, int nq, int nkv, int d, float scale, uint16_t *out, float *lse,
-                                       hipStream_t stream);
+                                       const int32_t *prefix_cu, const uint16_t *sk, const uint16_t *sv, int R,
+                                       int W, int Lp, int Ls, int Ls_cap, int nq, int nkv, int d, float scale,
+                                       uint16_t *out, float *lse, hipStream_t stream);
+
+hipError_t launch_last_token_gather(const void *src, const int32_t *cu, int num_seqs, int T, int64_t row_bytes,
+                                    void *dst, hipStream_t stream);
 
 hipError_t launch_suffix_reorder(const uint16_t *src_k, const uint16_t *src_v, uint16_t *dst_k, uint16_t *dst_v,
                                  const int32_t *parent, const int32_t *src_tok, int32_t *dst_tok, int R, int W,
@@ -45,6 +50,10 @@ hipError_t launch_beam_topk(const uint16_t *logits, const float *cum, int R, int
 // check kernel on `stream`, waits for it and returns the BGA_VIOLATION_* bits
 // found in *violations.
 hipError_t debug_check_prefill(const int32_t *cu, int B, int T, int max_seqlen, hipStream_t stream,
+                               uint32_t *violations);
+// cu_seqlens-style offsets of packed prompts; also flags a request with no key
+// at all (an empty prompt when suffix_len == 0)
+hipError_t debug_check_prompts(const int32_t *cu, int R, int T, int max_len, bool need_nonempty, hipStream_t stream,
                                uint32_t *violations);
 hipError_t debug_check_parents(const int32_t *parent, int n, int W, hipStream_t stream, uint32_t *violations);
 hipError_t debug_check_logits(const uint16_t *x, size_t n, hipStream_t stream, uint32_t *violations);

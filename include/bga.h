@@ -62,6 +62,7 @@ typedef enum {
 #define BGA_VIOLATION_MAX_SEQLEN 2u  /* a sequence is longer than max_seqlen */
 #define BGA_VIOLATION_PARENT 4u      /* a parent index outside [0, W) */
 #define BGA_VIOLATION_LOGITS 8u      /* a logit is inf or NaN */
+#define BGA_VIOLATION_NO_KEYS 16u    /* a request's beams would attend to no key (empty prompt, no suffix) */
 
 /* Caps (the article bounds its workloads to <= 400 beams, <= 5 generated
  * tokens and prompts averaging under 500 tokens, section 1.2). Each cap is
@@ -128,6 +129,47 @@ bga_status bga_shared_prefix_decode(const bga_bf16 *q, const bga_bf16 *prefix_k,
                                     int32_t suffix_cap, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
                                     hipStream_t stream);
+
+/*
+ * Shared-prefix beam decode with prompts of their own lengths, kept packed
+ * (article section 3.2 equation, with the prompt K/V in the packed layout the
+ * packed prefill of section 3.1 produces: the prefill's K/V output serves as
+ * the shared prefix with no copy).
+ *
+ *   prefix_k/v   [total_prefix_tokens, num_kv_heads, head_dim] bf16: request r's
+ *                prompt is rows prefix_cu[r] .. prefix_cu[r+1]-1
+ *   prefix_cu    [num_requests + 1] int32, device: prefix_cu[0] = 0,
+ *                non-decreasing, prefix_cu[R] = total_prefix_tokens, every prompt
+ *                <= BGA_MAX_SEQLEN tokens, and >= 1 token when suffix_len == 0
+ *                (preconditions, checked by the debug library)
+ *   every other argument, the layouts and the results as in
+ *   bga_shared_prefix_decode (which is this call with equal prompt lengths).
+ * A request whose prompt is empty attends to its beams' suffixes only.
+ */
+bga_status bga_shared_prefix_decode_packed(const bga_bf16 *q, const bga_bf16 *prefix_k, const bga_bf16 *prefix_v,
+                                           const int32_t *prefix_cu, int32_t total_prefix_tokens,
+                                           const bga_bf16 *suffix_k, const bga_bf16 *suffix_v,
+                                           int32_t num_requests, int32_t beam_width, int32_t suffix_len,
+                                           int32_t suffix_cap, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, float softmax_scale, bga_bf16 *out, float *lse,
+                                           hipStream_t stream);
+
+/*
+ * The last valid token of every packed sequence (article section 3.1: after
+ * packed attention the same sequence boundary selects each sequence's
+ * last-position hidden state, the input of the per-sample score head).
+ *
+ *   src        [total_tokens, row_bytes] (any element type: rows are copied
+ *              bit for bit), e.g. hidden states [T, H] or attention output
+ *              [T, Nq, D]
+ *   cu_seqlens [num_seqs + 1] int32, device, as in bga_packed_gqa_prefill
+ *   dst        [num_seqs, row_bytes]: row i = src row cu[i+1]-1; a
+ *              zero-length sequence gets a row of zeros
+ * row_bytes must be a positive multiple of 16; src and dst 16-byte aligned and
+ * not overlapping. Source rows are clamped to [0, total_tokens) on the device.
+ */
+bga_status bga_last_token_gather(const void *src, const int32_t *cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int64_t row_bytes, void *dst, hipStream_t stream);
 
 /*
  * Parent-index reorder (article sections 3.2 and 3.3: after candidate

@@ -158,3 +158,32 @@ def test_topk_noalloc_errors(m):
     # the library's own workspace holds 24 MiB: 8 x 400 beams with k_local 800 fit, 8 x 512 x 1024 do not
     assert m.beam_topk_workspace_size(8, 400, 151936, 800, 400) <= 24 << 20
     assert na(R=8, W=512, V=151936, kl=1024, kg=1024) == 5
+
+
+def test_decode_packed_errors(m):
+    def dp(q=P, pk=2 * P, pv=3 * P, cu=8 * P, tp=20, sk=4 * P, sv=5 * P, R=2, W=4, Ls=2, cap=3, nq=4, nkv=2, d=64,
+           out=6 * P, lse=7 * P):
+        return m.lib.bga_shared_prefix_decode_packed(q, pk, pv, cu, tp, sk, sv, R, W, Ls, cap, nq, nkv, d, 0.125, out,
+                                                     lse, None)
+    assert dp(tp=-1) == 2
+    assert dp(tp=0, Ls=0) == 2          # no key anywhere
+    assert dp(Ls=4) == 2
+    assert dp(W=513) == 3
+    assert dp(cu=None) == 1
+    assert dp(pk=None) == 1
+    assert dp(cu=8 * P + 2) == 4
+    assert dp(out=2 * P) == 6           # out overlaps the prompt K
+    assert dp(R=0) == 0
+
+
+def test_last_token_gather_errors(m):
+    def g(src=P, cu=2 * P, B=3, T=10, rb=256, dst=3 * P):
+        return m.lib.bga_last_token_gather(src, cu, B, T, rb, dst, None)
+    assert g(rb=100) == 2               # not a multiple of 16
+    assert g(rb=0) == 2
+    assert g(B=-1) == 2
+    assert g(cu=None) == 1
+    assert g(dst=None) == 1
+    assert g(src=P + 8) == 4
+    assert g(dst=P + 16 * 5) == 6       # dst inside src
+    assert g(B=0) == 0

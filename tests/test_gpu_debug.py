@@ -92,3 +92,16 @@ def test_topk_preconditions(dbg):
     import oracle
     ref = oracle.beam_topk(x.cpu(), None, 10, 5)
     assert np.array_equal(r["local_tokens"].cpu().numpy(), ref["local_tokens"])
+
+
+def test_packed_prompt_preconditions(dbg):
+    say("[debug] packed prompts: bad offsets, an empty prompt without a suffix")
+    c = wl.make_decode_case(3, 4, 1, 2, 4, 2, 64, seed=6, device=DEV)
+    pk = torch.zeros((20, 2, 64), dtype=torch.bfloat16, device=DEV)
+    bad = torch.tensor([0, 12, 8, 20], dtype=torch.int32, device=DEV)
+    expect_violation(lambda: dbg.shared_prefix_decode_packed(c.q, pk, pk, bad, c.suffix_k, c.suffix_v, 1), CU)
+    empty = torch.tensor([0, 12, 12, 20], dtype=torch.int32, device=DEV)
+    expect_violation(lambda: dbg.shared_prefix_decode_packed(c.q, pk, pk, empty, c.suffix_k, c.suffix_v, 0), 16)
+    dbg.shared_prefix_decode_packed(c.q, pk, pk, empty, c.suffix_k, c.suffix_v, 1)   # a suffix to attend to: fine
+    x = torch.zeros((20, 8), dtype=torch.float32, device=DEV)
+    expect_violation(lambda: dbg.last_token_gather(x, bad), CU)

@@ -140,3 +140,67 @@ def test_reorder_identity_and_bad_parent():
     bad[1, 2] = 99
     dk, dv = bga().suffix_reorder(sk, sv, bad, 3)
     assert torch.all(dk[1, 2] == 0) and torch.equal(dk[0], sk[0]) and torch.equal(dk[1, 3], sk[1, 3])
+
+
+# ---------------------------------------------------------------- prompts of their own lengths, packed
+
+def packed_prompts(lps, w, ls_cap, nq, nkv, d, seed):
+    c = wl.make_decode_case(len(lps), w, 1, ls_cap, nq, nkv, d, seed, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed + 1)
+    tp = int(sum(lps))
+    pk = wl.bf16_normal((tp, nkv, d), gen, DEV)
+    pv = wl.bf16_normal((tp, nkv, d), gen, DEV)
+    return c, pk, pv, wl.cu_seqlens_from_lengths(lps)
+
+
+@pytest.mark.parametrize("lps,w,ls,cap,nq,nkv,d", [
+    ((7, 0, 130, 64, 1), 5, 2, 3, 4, 2, 64),                  # an empty prompt, ragged and exact tiles
+    ((480, 455, 512, 300, 479, 1, 64, 200), 400, 3, 5, 16, 8, 128),   # long prompts of their own lengths, W 400
+    ((128, 96, 160, 33) * 8, 100, 4, 4, 16, 8, 64),           # 32 short-prompt requests, W 100
+    ((65, 0, 17), 130, 1, 2, 4, 4, 128),                      # group 1, two slots of beams per workgroup
+    ((5, 9), 9, 0, 2, 16, 1, 128),                            # no suffix: prompts only
+])
+def test_packed_prompt_decode(lps, w, ls, cap, nq, nkv, d):
+    c, pk, pv, cu = packed_prompts(lps, w, cap, nq, nkv, d, seed=len(lps) * 100 + w)
+    say(f"[decode packed] R={len(lps)} W={w} prompts {lps[:8]} Ls={ls}/{cap} nq={nq} nkv={nkv} d={d}")
+    out, lse = bga().shared_prefix_decode_packed(c.q, pk, pv, torch.from_numpy(cu).to(DEV), c.suffix_k, c.suffix_v, ls)
+    torch.cuda.synchronize()
+    ro, rl = oracle.shared_prefix_decode_packed(c.q.cpu(), pk.cpu(), pv.cpu(), cu, c.suffix_k.cpu(), c.suffix_v.cpu(),
+                                                ls)
+    e = check_bf16(out, ro, "packed prompts out")
+    l_ = check_lse(lse, rl, "packed prompts lse")
+    say(f"    max |out err| {e:.2e}  max |lse err| {l_:.2e}")
+
+
+def test_packed_prompts_of_equal_length_equal_the_strided_layout():
+    """With every prompt of the same length the packed call is the strided call, bit for bit: the prefill's
+    packed K/V of the prompts serves as the shared prefix unchanged."""
+    c = wl.make_decode_case(4, 37, 90, 3, 8, 2, 64, seed=11, device=DEV)
+    cu = torch.arange(0, 5 * 90, 90, dtype=torch.int32, device=DEV)
+    o1, l1 = bga().shared_prefix_decode(c.q, c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, 2)
+    o2, l2 = bga().shared_prefix_decode_packed(c.q, c.prefix_k.view(-1, 2, 64), c.prefix_v.view(-1, 2, 64), cu,
+                                               c.suffix_k, c.suffix_v, 2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- last valid token of each sequence
+
+@pytest.mark.parametrize("lengths,row_shape,dtype", [
+    ([3, 0, 1, 7, 0, 2], (16, 128), torch.bfloat16),
+    (wl.lengths_uniform(15, 64, 480, 1), (16, 128), torch.bfloat16),
+    ([1] * 33, (1000,), torch.float32),
+    ([5, 300, 0, 11], (8192,), torch.float32),      # 32 KB rows: several workgroups per row
+    ([0, 0], (8,), torch.float16),
+])
+def test_last_token_gather(lengths, row_shape, dtype):
+    cu = wl.cu_seqlens_from_lengths(lengths)
+    t = int(cu[-1])
+    g = torch.Generator(device=DEV)
+    g.manual_seed(t)
+    x = torch.randn((t,) + row_shape, generator=g, device=DEV).to(dtype)
+    say(f"[gather] B={len(lengths)} T={t} row {row_shape} {dtype}")
+    y = bga().last_token_gather(x, torch.from_numpy(cu).to(DEV))
+    ref = oracle.last_token_gather(x.cpu().view(torch.int16 if x.element_size() == 2 else torch.int32).numpy(), cu)
+    got = y.cpu().view(torch.int16 if x.element_size() == 2 else torch.int32).numpy()
+    assert np.array_equal(got, ref)
