@@ -95,3 +95,38 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     r = run_pins(tmp_path, text.replace(old, new))
     # exit status 1: some pin failed (not a crash, a collection error or an interrupt)
     assert r.returncode == 1, f"'{name}' survived the pins:\n" + r.stdout[-3000:] + r.stderr[-2000:]
+
+
+LOOP_SRC = os.path.join(ROOT, "oracle", "beam_loop.py")
+LOOP_PINS = os.path.join(ROOT, "tests", "test_oracle_beam_loop.py")
+LOOP_MUTANTS = [
+    ("stop-token candidates also continue", "        elif len(parents) < W:", "        if len(parents) < W:"),
+    ("finished history of beam 0", "finished.append(Finished(float(sc), list(histories[par]) + [tok]))",
+     "finished.append(Finished(float(sc), list(histories[0]) + [tok]))"),
+    ("K/V copied from the slot, not the parent", "new_k.append([full_k[r][p].copy() for p in par])",
+     "new_k.append([full_k[r][min(b, len(full_k[r]) - 1)].copy() for b in range(len(par))])"),
+    ("final ranking ascending", "entries.sort(key=lambda e: (-e[0], e[1]))", "entries.sort(key=lambda e: (e[0], e[1]))"),
+    ("current token's K not appended", "full_k[r][b] = np.concatenate([full_k[r][b], kn[r, b][None]])",
+     "full_k[r][b] = full_k[r][b]"),
+]
+
+
+def test_loop_pins_pass_on_an_unmodified_copy(tmp_path):
+    src = tmp_path / "beam_loop.py"
+    src.write_text(open(LOOP_SRC).read())
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", LOOP_PINS], cwd=ROOT,
+                       env=dict(os.environ, BGA_ORACLE_BEAM_LOOP=str(src)), capture_output=True, text=True,
+                       timeout=900)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name,old,new", LOOP_MUTANTS, ids=[m[0] for m in LOOP_MUTANTS])
+def test_loop_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(LOOP_SRC).read()
+    assert text.count(old) == 1, f"mutation site of '{name}' not unique"
+    src = tmp_path / "beam_loop.py"
+    src.write_text(text.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", LOOP_PINS], cwd=ROOT,
+                       env=dict(os.environ, BGA_ORACLE_BEAM_LOOP=str(src)), capture_output=True, text=True,
+                       timeout=900)
+    assert r.returncode == 1, f"'{name}' survived the pins:\n" + r.stdout[-3000:] + r.stderr[-2000:]
