@@ -31,7 +31,8 @@ STATUS_NAMES = {0: "BGA_OK", 1: "BGA_ERR_NULL", 2: "BGA_ERR_SHAPE", 3: "BGA_ERR_
 EXPORTS = ("bga_packed_gqa_prefill", "bga_shared_prefix_decode", "bga_suffix_reorder",
            "bga_beam_topk_workspace_size", "bga_beam_topk", "bga_status_string", "bga_last_hip_error",
            "bga_version", "bga_debug_build", "bga_last_violations", "bga_beam_topk_noalloc",
-           "bga_shared_prefix_decode_packed", "bga_last_token_gather")
+           "bga_shared_prefix_decode_packed", "bga_last_token_gather", "bga_beam_advance", "bga_suffix_append",
+           "bga_beam_finalize")
 
 
 class BgaError(RuntimeError):
@@ -51,6 +52,9 @@ def load_library(path: str = LIB_PATH):
     L.bga_shared_prefix_decode_packed.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32, f32, P,
                                                   P, P]
     L.bga_last_token_gather.argtypes = [P, P, i32, i32, ctypes.c_int64, P, P]
+    L.bga_beam_advance.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, i32, P, P, P, P, P, P, i32, P]
+    L.bga_suffix_append.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+    L.bga_beam_finalize.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P]
     L.bga_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, P]
     L.bga_beam_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.bga_beam_topk_workspace_size.restype = sz
@@ -64,7 +68,8 @@ def load_library(path: str = LIB_PATH):
     L.bga_last_violations.argtypes = []
     L.bga_last_violations.restype = ctypes.c_uint32
     for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_shared_prefix_decode_packed,
-              L.bga_last_token_gather, L.bga_suffix_reorder, L.bga_beam_topk,
+              L.bga_last_token_gather, L.bga_suffix_reorder, L.bga_beam_topk, L.bga_beam_advance,
+              L.bga_suffix_append, L.bga_beam_finalize,
               L.bga_beam_topk_noalloc, L.bga_last_hip_error, L.bga_version, L.bga_debug_build):
         f.restype = i32
     return L
@@ -320,3 +325,77 @@ def beam_topk_noalloc(logits, cum_scores, k_local: int, k_global: int, out: dict
                                    _ptr(res.get("row_lse")), _stream(logits))
     _check(st, "bga_beam_topk_noalloc")
     return res
+
+
+def beam_advance(cand_tokens, cand_parents, cand_scores, beam_width: int, stop_token: int, step: int, tokens_in,
+                 tokens_out, parents_out, cum_out, pool: dict):
+    """The 2W stop-token rule of one beam-search step (bga_beam_advance). cand_* [R, 2W] (best first);
+    tokens_in [R, W_in, tok_cap], tokens_out [R, W, tok_cap] int32; parents_out [R, W] int32, cum_out [R, W] fp32;
+    pool = dict(scores [R, P] fp32, lengths [R, P] int32, tokens [R, P, tok_cap] int32, count [R] int32)."""
+    _need(cand_tokens, "cand_tokens", torch.int32, ndim=2)
+    dev = cand_tokens.device
+    r, k2 = cand_tokens.shape
+    w = int(beam_width)
+    if k2 != 2 * w:
+        raise ValueError(f"expected 2W = {2 * w} candidates per request, got {k2}")
+    _need(cand_parents, "cand_parents", torch.int32, dev, shape=(r, k2))
+    _need(cand_scores, "cand_scores", torch.float32, dev, shape=(r, k2))
+    _need(tokens_in, "tokens_in", torch.int32, dev, 3)
+    w_in, tok_cap = tokens_in.shape[1], tokens_in.shape[2]
+    if tokens_in.shape[0] != r:
+        raise ValueError("tokens_in must be [R, W_in, tok_cap]")
+    _need(tokens_out, "tokens_out", torch.int32, dev, shape=(r, w, tok_cap))
+    _need(parents_out, "parents_out", torch.int32, dev, shape=(r, w))
+    _need(cum_out, "cum_out", torch.float32, dev, shape=(r, w))
+    p = pool["scores"].shape[1] if isinstance(pool.get("scores"), torch.Tensor) else 0
+    _need(pool["scores"], "pool scores", torch.float32, dev, shape=(r, p))
+    _need(pool["lengths"], "pool lengths", torch.int32, dev, shape=(r, p))
+    _need(pool["tokens"], "pool tokens", torch.int32, dev, shape=(r, p, tok_cap))
+    _need(pool["count"], "pool count", torch.int32, dev, shape=(r,))
+    st = lib.bga_beam_advance(_ptr(cand_tokens), _ptr(cand_parents), _ptr(cand_scores), r, w_in, w, int(stop_token),
+                              int(step), _ptr(tokens_in), _ptr(tokens_out), tok_cap, _ptr(parents_out), _ptr(cum_out),
+                              _ptr(pool["scores"]), _ptr(pool["lengths"]), _ptr(pool["tokens"]), _ptr(pool["count"]),
+                              p, _stream(cand_tokens))
+    _check(st, "bga_beam_advance")
+
+
+def suffix_append(new_k, new_v, suffix_k, suffix_v, pos: int):
+    """new_k/new_v [R, W, Nkv, D] into suffix position pos of suffix_k/suffix_v [R, W, cap, Nkv, D] (bf16)."""
+    _need(suffix_k, "suffix_k", torch.bfloat16, ndim=5)
+    dev = suffix_k.device
+    r, w, cap, nkv, d = suffix_k.shape
+    _need(suffix_v, "suffix_v", torch.bfloat16, dev, shape=suffix_k.shape)
+    _need(new_k, "new_k", torch.bfloat16, dev, shape=(r, w, nkv, d))
+    _need(new_v, "new_v", torch.bfloat16, dev, shape=(r, w, nkv, d))
+    st = lib.bga_suffix_append(_ptr(new_k), _ptr(new_v), _ptr(suffix_k), _ptr(suffix_v), r, w, int(pos), cap, nkv, d,
+                               _stream(suffix_k))
+    _check(st, "bga_suffix_append")
+
+
+def beam_finalize(pool: dict, cum, tokens, length: int, out: dict | None = None):
+    """Finished pool + last beams ranked by score, best first (bga_beam_finalize). Returns
+    dict(scores [R, P+W], lengths [R, P+W], tokens [R, P+W, tok_cap], count [R])."""
+    _need(cum, "cum", torch.float32, ndim=2)
+    dev = cum.device
+    r, w = cum.shape
+    _need(tokens, "tokens", torch.int32, dev, 3)
+    tok_cap = tokens.shape[2]
+    if tokens.shape[:2] != (r, w):
+        raise ValueError("tokens must be [R, W, tok_cap]")
+    p = pool["scores"].shape[1]
+    _need(pool["scores"], "pool scores", torch.float32, dev, shape=(r, p))
+    _need(pool["lengths"], "pool lengths", torch.int32, dev, shape=(r, p))
+    _need(pool["tokens"], "pool tokens", torch.int32, dev, shape=(r, p, tok_cap))
+    _need(pool["count"], "pool count", torch.int32, dev, shape=(r,))
+    out = {} if out is None else out
+    shapes = {"scores": ((r, p + w), torch.float32), "lengths": ((r, p + w), torch.int32),
+              "tokens": ((r, p + w, tok_cap), torch.int32), "count": ((r,), torch.int32)}
+    for key, (shape, dtype) in shapes.items():
+        if key not in out:
+            out[key] = torch.empty(shape, dtype=dtype, device=dev)
+        _need(out[key], key, dtype, dev, shape=shape)
+    st = lib.bga_beam_finalize(_ptr(pool["scores"]), _ptr(pool["lengths"]), _ptr(pool["tokens"]), _ptr(pool["count"]),
+                               p, _ptr(cum), _ptr(tokens), r, w, int(length), tok_cap, _ptr(out["scores"]),
+                               _ptr(out["lengths"]), _ptr(out["tokens"]), _ptr(out["count"]), _stream(cum))
+    _check(st, "bga_beam_finalize")
+    return out

@@ -326,6 +326,77 @@ bga_status bga_beam_topk_noalloc(const bga_bf16 *logits, const float *cum_scores
                                             local_scores, row_lse, workspace, stream));
 }
 
+bga_status bga_beam_advance(const int32_t *cand_tokens, const int32_t *cand_parents, const float *cand_scores,
+                            int32_t num_requests, int32_t num_src_beams, int32_t beam_width, int32_t stop_token,
+                            int32_t step, const int32_t *tokens_in, int32_t *tokens_out, int32_t tok_cap,
+                            int32_t *parents_out, float *cum_out, float *pool_scores, int32_t *pool_lengths,
+                            int32_t *pool_tokens, int32_t *pool_count, int32_t pool_cap, hipStream_t stream)
+{
+    if (num_requests < 0 || beam_width < 1 || num_src_beams < 1 || num_src_beams > beam_width || step < 0 ||
+        step >= tok_cap || pool_cap < 1)
+        return BGA_ERR_SHAPE;
+    if (beam_width > BGA_MAX_BEAMS) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * pool_cap * tok_cap > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
+    if (num_requests == 0) return BGA_OK;
+    if (!cand_tokens || !cand_parents || !cand_scores || !tokens_in || !tokens_out || !parents_out || !cum_out ||
+        !pool_scores || !pool_lengths || !pool_tokens || !pool_count)
+        return BGA_ERR_NULL;
+    const void *ptrs[] = {cand_tokens, cand_parents, cand_scores, tokens_in, tokens_out, parents_out, cum_out,
+                          pool_scores, pool_lengths, pool_tokens, pool_count};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4)) return BGA_ERR_ALIGN;
+    const size_t tin = (size_t)num_requests * num_src_beams * tok_cap * 4;
+    const size_t tout = (size_t)num_requests * beam_width * tok_cap * 4;
+    if (overlap(tokens_out, tout, tokens_in, tin)) return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_beam_advance(cand_tokens, cand_parents, cand_scores, num_requests, num_src_beams,
+                                               beam_width, stop_token, step, tokens_in, tokens_out, tok_cap,
+                                               parents_out, cum_out, pool_scores, pool_lengths, pool_tokens,
+                                               pool_count, pool_cap, stream));
+}
+
+bga_status bga_suffix_append(const bga_bf16 *new_k, const bga_bf16 *new_v, bga_bf16 *suffix_k, bga_bf16 *suffix_v,
+                             int32_t num_requests, int32_t beam_width, int32_t pos, int32_t suffix_cap,
+                             int32_t num_kv_heads, int32_t head_dim, hipStream_t stream)
+{
+    if (num_requests < 0 || beam_width < 0 || pos < 0 || pos >= suffix_cap || num_kv_heads <= 0) return BGA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
+    if (beam_width > BGA_MAX_BEAMS || suffix_cap > BGA_MAX_SUFFIX) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * beam_width > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
+    if (num_requests == 0 || beam_width == 0) return BGA_OK;
+    if (!new_k || !new_v || !suffix_k || !suffix_v) return BGA_ERR_NULL;
+    if (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(suffix_k, 16) || !aligned(suffix_v, 16))
+        return BGA_ERR_ALIGN;
+    const size_t nb = (size_t)num_requests * beam_width * num_kv_heads * head_dim * 2;
+    const size_t sb = nb * suffix_cap;
+    if (overlap(suffix_k, sb, new_k, nb) || overlap(suffix_k, sb, new_v, nb) || overlap(suffix_v, sb, new_k, nb) ||
+        overlap(suffix_v, sb, new_v, nb) || overlap(suffix_k, sb, suffix_v, sb))
+        return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_suffix_append(new_k, new_v, suffix_k, suffix_v, num_requests, beam_width, pos,
+                                                suffix_cap, num_kv_heads, head_dim, stream));
+}
+
+bga_status bga_beam_finalize(const float *pool_scores, const int32_t *pool_lengths, const int32_t *pool_tokens,
+                             const int32_t *pool_count, int32_t pool_cap, const float *cum, const int32_t *tokens,
+                             int32_t num_requests, int32_t beam_width, int32_t length, int32_t tok_cap,
+                             float *final_scores, int32_t *final_lengths, int32_t *final_tokens,
+                             int32_t *final_count, hipStream_t stream)
+{
+    if (num_requests < 0 || beam_width < 1 || pool_cap < 1 || length < 1 || length > tok_cap) return BGA_ERR_SHAPE;
+    if ((int64_t)pool_cap + beam_width > bga::beam_final_max()) return BGA_ERR_UNSUPPORTED;
+    if ((int64_t)num_requests * (pool_cap + beam_width) * tok_cap > 0x7fffffff) return BGA_ERR_UNSUPPORTED;
+    if (num_requests == 0) return BGA_OK;
+    if (!pool_scores || !pool_lengths || !pool_tokens || !pool_count || !cum || !tokens || !final_scores ||
+        !final_lengths || !final_tokens || !final_count)
+        return BGA_ERR_NULL;
+    const void *ptrs[] = {pool_scores, pool_lengths, pool_tokens, pool_count, cum, tokens,
+                          final_scores, final_lengths, final_tokens, final_count};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4)) return BGA_ERR_ALIGN;
+    return hip_status(bga::launch_beam_finalize(pool_scores, pool_lengths, pool_tokens, pool_count, pool_cap, cum,
+                                                tokens, num_requests, beam_width, length, tok_cap, final_scores,
+                                                final_lengths, final_tokens, final_count, stream));
+}
+
 const char *bga_status_string(bga_status s)
 {
     switch (s) {

@@ -45,6 +45,20 @@ hipError_t launch_beam_topk(const uint16_t *logits, const float *cum, int R, int
                             int32_t *local_tok, float *local_score, float *row_lse, void *workspace,
                             hipStream_t stream);
 
+// Beam-search state update (beam.hip).
+hipError_t launch_beam_advance(const int32_t *cand_tok, const int32_t *cand_par, const float *cand_score, int R,
+                               int W_in, int W, int stop, int step, const int32_t *tok_in, int32_t *tok_out,
+                               int tok_cap, int32_t *parents_out, float *cum_out, float *pool_score,
+                               int32_t *pool_len, int32_t *pool_tok, int32_t *pool_count, int pool_cap,
+                               hipStream_t stream);
+hipError_t launch_suffix_append(const uint16_t *new_k, const uint16_t *new_v, uint16_t *sk, uint16_t *sv, int R, int W,
+                                int pos, int cap, int nkv, int d, hipStream_t stream);
+int beam_final_max();
+hipError_t launch_beam_finalize(const float *pool_score, const int32_t *pool_len, const int32_t *pool_tok,
+                                const int32_t *pool_count, int pool_cap, const float *cum, const int32_t *tok, int R,
+                                int W, int len, int tok_cap, float *final_score, int32_t *final_len,
+                                int32_t *final_tok, int32_t *final_count, hipStream_t stream);
+
 #ifdef BGA_DEBUG
 // Debug build: device-side precondition checks (debug_checks.hip). Each runs a
 // check kernel on `stream`, waits for it and returns the BGA_VIOLATION_* bits

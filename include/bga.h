@@ -193,6 +193,80 @@ bga_status bga_suffix_reorder(const bga_bf16 *src_k, const bga_bf16 *src_v, bga_
                               int32_t num_kv_heads, int32_t head_dim, int32_t num_tokens, int32_t tok_cap,
                               hipStream_t stream);
 
+/*
+ * Fixed-depth beam search state update (article section 2.3, the loop
+ * "prompt prefill -> first-step initialisation -> (N_gen - 1) x [decode ->
+ * per-beam selection -> cumulative merge -> parent update -> token and suffix
+ * K/V reorder] -> final candidates and scores"; section 3.3: 2W global
+ * candidates are kept so that hypotheses that produced the stop token finish
+ * while W beams continue). One step of the loop is
+ *     bga_suffix_append (the current token's K/V) -> bga_shared_prefix_decode
+ *     (or _packed) -> [the model: logits] -> bga_beam_topk with k_local =
+ *     k_global = 2W -> bga_beam_advance -> bga_suffix_reorder by the new parents;
+ * the first step (step = 0) selects from the prompt's last-token logits with
+ * num_src_beams = 1 and no cumulative scores, and bga_beam_finalize ranks the
+ * result after the last step.
+ */
+
+/*
+ * The 2W rule on the global candidates of one step, per request. Of the 2W
+ * candidates (bga_beam_topk output with k_global = 2W, best first), every one
+ * whose token is stop_token becomes a finished hypothesis: appended to the
+ * request's pool with its score, length step + 1 and tokens (its source beam's
+ * step tokens, then stop_token). The first W others become the new beams in
+ * candidate order: parents_out, cum_out (their scores) and tokens_out (the
+ * source beam's step tokens, then the new token). Each source beam's candidates
+ * hold distinct tokens, so at most num_src_beams <= W of them are stop tokens
+ * and the W beams always fill.
+ *
+ *   cand_tokens, cand_parents [R, 2W] int32; cand_scores [R, 2W] fp32
+ *   tokens_in  [R, num_src_beams, tok_cap] int32 (positions < step are read)
+ *   tokens_out [R, W, tok_cap] (positions <= step are written); must not
+ *              overlap tokens_in
+ *   parents_out [R, W] int32; cum_out [R, W] fp32
+ *   pool_scores [R, pool_cap] fp32, pool_lengths [R, pool_cap] int32,
+ *   pool_tokens [R, pool_cap, tok_cap] int32, pool_count [R] int32: the
+ *              finished pool. At step 0 the pool is taken as empty (pool_count
+ *              need not be initialised); later steps append after pool_count.
+ *              Hypotheses beyond pool_cap are dropped (W x N_gen always
+ *              suffices).
+ * Requires 1 <= W <= BGA_MAX_BEAMS, 1 <= num_src_beams <= W, 0 <= step and
+ * step < tok_cap, pool_cap >= 1; all pointers 4-byte aligned.
+ */
+bga_status bga_beam_advance(const int32_t *cand_tokens, const int32_t *cand_parents, const float *cand_scores,
+                            int32_t num_requests, int32_t num_src_beams, int32_t beam_width, int32_t stop_token,
+                            int32_t step, const int32_t *tokens_in, int32_t *tokens_out, int32_t tok_cap,
+                            int32_t *parents_out, float *cum_out, float *pool_scores, int32_t *pool_lengths,
+                            int32_t *pool_tokens, int32_t *pool_count, int32_t pool_cap, hipStream_t stream);
+
+/*
+ * The current token's K/V of every beam into suffix position `pos` (the K/V
+ * projection of the token each beam selected at the previous step).
+ *   new_k, new_v [R, W, num_kv_heads, head_dim] bf16
+ *   suffix_k, suffix_v [R, W, suffix_cap, num_kv_heads, head_dim] bf16, written
+ *   at position pos only. Requires 0 <= pos < suffix_cap <= BGA_MAX_SUFFIX;
+ *   16-byte aligned; new and suffix buffers must not overlap.
+ */
+bga_status bga_suffix_append(const bga_bf16 *new_k, const bga_bf16 *new_v, bga_bf16 *suffix_k, bga_bf16 *suffix_v,
+                             int32_t num_requests, int32_t beam_width, int32_t pos, int32_t suffix_cap,
+                             int32_t num_kv_heads, int32_t head_dim, hipStream_t stream);
+
+/*
+ * Final candidates and scores: per request, the finished pool and the last W
+ * beams (cum [R, W], tokens [R, W, tok_cap] of length `length`) ranked together
+ * by score, best first (equal scores: finished before beams, earlier before
+ * later, lower beam first; no length normalisation).
+ *   final_scores [R, pool_cap + W] fp32, final_lengths [R, pool_cap + W] int32,
+ *   final_tokens [R, pool_cap + W, tok_cap] int32, final_count [R] int32
+ *   (= pool_count + W; entries past it are not written).
+ * Requires pool_cap + W <= 8192, 1 <= length <= tok_cap.
+ */
+bga_status bga_beam_finalize(const float *pool_scores, const int32_t *pool_lengths, const int32_t *pool_tokens,
+                             const int32_t *pool_count, int32_t pool_cap, const float *cum, const int32_t *tokens,
+                             int32_t num_requests, int32_t beam_width, int32_t length, int32_t tok_cap,
+                             float *final_scores, int32_t *final_lengths, int32_t *final_tokens,
+                             int32_t *final_count, hipStream_t stream);
+
 /* Bytes of device workspace bga_beam_topk needs for these sizes (0 on bad sizes). */
 size_t bga_beam_topk_workspace_size(int32_t num_requests, int32_t num_src_beams, int32_t vocab,
                                     int32_t k_local, int32_t k_global);

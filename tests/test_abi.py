@@ -187,3 +187,34 @@ def test_last_token_gather_errors(m):
     assert g(src=P + 8) == 4
     assert g(dst=P + 16 * 5) == 6       # dst inside src
     assert g(B=0) == 0
+
+
+def test_beam_state_update_errors(m):
+    def adv(R=2, Win=4, W=4, step=1, tc=5, pc=8, ti=P, to=2 * P):
+        return m.lib.bga_beam_advance(3 * P, 4 * P, 5 * P, R, Win, W, 7, step, ti, to, tc, 6 * P, 7 * P, 8 * P, 9 * P,
+                                      10 * P, 11 * P, pc, None)
+    assert adv(Win=5) == 2              # more source beams than beams
+    assert adv(step=5) == 2             # no room for the new token
+    assert adv(pc=0) == 2
+    assert adv(W=513, Win=1) == 3
+    assert adv(ti=None) == 1
+    assert adv(to=P + 2) == 4
+    assert adv(to=P) == 6               # new token lists over the old ones
+    assert adv(R=0) == 0
+
+    def app(R=2, W=4, pos=1, cap=3, nk=P, sk=2 * P):
+        return m.lib.bga_suffix_append(nk, 3 * P, sk, 4 * P, R, W, pos, cap, 2, 64, None)
+    assert app(pos=3) == 2
+    assert app(cap=17, pos=1) == 3
+    assert app(nk=None) == 1
+    assert app(sk=2 * P + 4) == 4
+    assert app(nk=2 * P) == 6
+    assert app(W=0) == 0
+
+    def fin(R=2, W=4, pc=8, ln=3, tc=5):
+        return m.lib.bga_beam_finalize(P, 2 * P, 3 * P, 4 * P, pc, 5 * P, 6 * P, R, W, ln, tc, 7 * P, 8 * P, 9 * P,
+                                       10 * P, None)
+    assert fin(ln=6) == 2
+    assert fin(ln=0) == 2
+    assert fin(pc=8190) == 3            # more than 8192 entries to rank
+    assert fin(R=0) == 0
