@@ -55,6 +55,12 @@ def lib():
         L.oracle_beam_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
         L.oracle_beam_topk_given_lse.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
         L.oracle_num_threads.argtypes = [i32]
+        L.oracle_e4m3_encode.argtypes = [f64]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = f64
+        L.oracle_swiglu_quant.argtypes = [P, i32, i32, P, P, P, P, i32]
+        L.oracle_swiglu_quant.restype = i32
         for f in (L.oracle_packed_prefill, L.oracle_shared_prefix_decode, L.oracle_shared_prefix_decode_packed,
                   L.oracle_last_token_gather, L.oracle_suffix_reorder,
                   L.oracle_beam_topk, L.oracle_beam_topk_given_lse, L.oracle_num_threads):
@@ -196,4 +202,32 @@ def beam_topk(logits, cum, k_local, k_global, nthreads: int = 0, row_lse=None):
                                               _p(out["row_lse64"]), nthreads)
     if rc:
         raise ValueError(f"oracle_beam_topk rejected its arguments ({rc})")
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of float64 values: round to nearest even, saturating at 448."""
+    x = np.asarray(x, np.float64)
+    f = lib().oracle_e4m3_encode
+    return np.array([f(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, np.uint8)
+    f = lib().oracle_e4m3_decode
+    return np.array([f(int(v)) for v in c.ravel()], np.float64).reshape(c.shape)
+
+
+def swiglu_quant(gate_up, nthreads: int = 0):
+    """Fused SwiGLU requantisation of [T, 2I] bf16 (gate | up). Returns dict(codes uint8 [T, I],
+    scale fp64 [T], h fp64 [T, I] (SiLU(gate) * up), x fp64 [T, I] (h / scale))."""
+    g = _bits(gate_up)
+    t, two_i = g.shape
+    i = two_i // 2
+    out = dict(codes=np.zeros((t, i), np.uint8), scale=np.zeros(t, np.float64), h=np.zeros((t, i), np.float64),
+               x=np.zeros((t, i), np.float64))
+    rc = lib().oracle_swiglu_quant(_p(g), t, i, _p(out["codes"]), _p(out["scale"]), _p(out["h"]), _p(out["x"]),
+                                   nthreads)
+    if rc:
+        raise ValueError(f"oracle_swiglu_quant rejected its arguments ({rc})")
     return out

@@ -389,3 +389,75 @@ int32_t oracle_beam_topk_given_lse(const uint16_t *logits, const float *cum, con
     free(lsc);
     return 0;
 }
+
+/* ---- selective FP8: fused SwiGLU requantisation (article section 3.4) ---- */
+
+/*
+ * OCP FP8 E4M3 ("e4m3fn") code of x: 1 sign bit, 4 exponent bits (bias 7),
+ * 3 mantissa bits; no infinities; the all-ones exponent with mantissa 111 is
+ * NaN, so the largest finite magnitude is 1.75 * 2^8 = 448; subnormals are
+ * m/8 * 2^-6. Round to nearest, ties to even; magnitudes that round above 448
+ * saturate to 448 (the requantisation never produces NaN).
+ */
+uint8_t oracle_e4m3_encode(double x)
+{
+    const uint8_t sign = (x < 0 || (x == 0 && signbit(x))) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a >= 464.0) return sign | 0x7E;   /* 464 is the midpoint between 448 and the next step, 480 */
+    int e = a > 0 ? (int)floor(log2(a)) : -6;
+    if (e < -6) e = -6;
+    /* a / 2^(e-3) is exact in double; rint rounds to nearest even */
+    double q = rint(ldexp(a, 3 - e));
+    if (q >= 16.0) {   /* rounded up to the next binade */
+        q = 8.0;
+        e += 1;
+    }
+    if (q < 8.0) return sign | (uint8_t)q;                 /* subnormal (e == -6) or zero */
+    if (e > 8 || (e == 8 && q > 14.0)) return sign | 0x7E;  /* above 448: saturate */
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+/* value of an E4M3 code (for the tests) */
+double oracle_e4m3_decode(uint8_t c)
+{
+    const double s = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return s * ldexp(m / 8.0, -6);
+    return s * ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/*
+ * Per token (one row of the Gate/Up projection's output [T, 2I], gate in
+ * columns 0..I-1 and up in I..2I-1): h = SiLU(gate) * up = gate / (1 + e^-gate)
+ * * up; amax = max |h|; scale = max(amax, 1e-12) / 448; codes = E4M3(h /
+ * scale). fp64 throughout (the definition; the kernel computes in fp32). Also
+ * returns h and h / scale for the tests.
+ */
+int32_t oracle_swiglu_quant(const uint16_t *gate_up, int32_t T, int32_t I, uint8_t *codes, double *scale,
+                            double *h_out, double *x_out, int32_t nthreads)
+{
+    if (!gate_up || !codes || !scale) return 1;
+    if (T < 0 || I <= 0) return 2;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(pick_threads(nthreads))
+    for (int32_t t = 0; t < T; ++t) {
+        const uint16_t *row = gate_up + (int64_t)t * 2 * I;
+        double *h = malloc(sizeof(double) * I);
+        double amax = 0.0;
+        for (int32_t j = 0; j < I; ++j) {
+            const double g = widen(row[j]), u = widen(row[I + j]);
+            h[j] = g / (1.0 + exp(-g)) * u;
+            if (fabs(h[j]) > amax) amax = fabs(h[j]);
+        }
+        const double sc = (amax > 1e-12 ? amax : 1e-12) / 448.0;
+        scale[t] = sc;
+        for (int32_t j = 0; j < I; ++j) {
+            const double x = h[j] / sc;
+            codes[(int64_t)t * I + j] = oracle_e4m3_encode(x);
+            if (h_out) h_out[(int64_t)t * I + j] = h[j];
+            if (x_out) x_out[(int64_t)t * I + j] = x;
+        }
+        free(h);
+    }
+    return 0;
+}

@@ -17,6 +17,7 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+FP8_PINS = os.path.join(ROOT, "tests", "test_oracle_fp8.py")
 
 # (name, text of oracle.c, the mistaken text)
 ATTEND_CALL = "attend(qq, keys, vals, t + 1, d, scale, s, o, &lse[row]);"
@@ -52,6 +53,13 @@ MUTANTS = [
      "const int64_t last = (int64_t)cu[i];"),
     ("empty sequence not zeroed", "memset(dst + (int64_t)i * row_bytes, 0, (size_t)row_bytes);",
      "memset(dst + (int64_t)i * row_bytes, 1, (size_t)row_bytes);"),
+    # selective FP8 requantisation
+    ("E4M3 ties away from zero", "double q = rint(ldexp(a, 3 - e));", "double q = floor(ldexp(a, 3 - e) + 0.5);"),
+    ("E4M3 exponent bias 8", "return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));",
+     "return sign | (uint8_t)(((e + 8) << 3) | ((int)q - 8));"),
+    ("SiLU without the gate factor", "h[j] = g / (1.0 + exp(-g)) * u;", "h[j] = 1.0 / (1.0 + exp(-g)) * u;"),
+    ("scale from the E5M2 maximum", "const double sc = (amax > 1e-12 ? amax : 1e-12) / 448.0;",
+     "const double sc = (amax > 1e-12 ? amax : 1e-12) / 57344.0;"),
     # suffix reorder
     ("reorder scatters", "dst_k[((r * W + b) * Ls_cap + j) * row + e] = src_k[((r * W + p) * Ls_cap + j) * row + e];",
      "dst_k[((r * W + p) * Ls_cap + j) * row + e] = src_k[((r * W + b) * Ls_cap + j) * row + e];"),
@@ -80,7 +88,7 @@ def run_pins(tmp_path, source_text):
     so = oracle.build(src=str(src), out=str(tmp_path / "liboracle_copy.so"))
     env = dict(os.environ, BGA_ORACLE_LIB=so)
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
-                           PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+                           PINS, FP8_PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
 
 
 def test_pins_pass_on_an_unmodified_copy(tmp_path):
