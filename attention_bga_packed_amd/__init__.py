@@ -22,4 +22,5 @@ from ._binding import (  # noqa: F401
     shared_prefix_decode,
     shared_prefix_decode_packed,
     suffix_reorder,
+    swiglu_quant_e4m3,
 )

@@ -32,7 +32,7 @@ EXPORTS = ("bga_packed_gqa_prefill", "bga_shared_prefix_decode", "bga_suffix_reo
            "bga_beam_topk_workspace_size", "bga_beam_topk", "bga_status_string", "bga_last_hip_error",
            "bga_version", "bga_debug_build", "bga_last_violations", "bga_beam_topk_noalloc",
            "bga_shared_prefix_decode_packed", "bga_last_token_gather", "bga_beam_advance", "bga_suffix_append",
-           "bga_beam_finalize")
+           "bga_beam_finalize", "bga_swiglu_quant_e4m3")
 
 
 class BgaError(RuntimeError):
@@ -54,6 +54,7 @@ def load_library(path: str = LIB_PATH):
     L.bga_last_token_gather.argtypes = [P, P, i32, i32, ctypes.c_int64, P, P]
     L.bga_beam_advance.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, i32, P, P, P, P, P, P, i32, P]
     L.bga_suffix_append.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+    L.bga_swiglu_quant_e4m3.argtypes = [P, i32, i32, P, P, P]
     L.bga_beam_finalize.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, P]
     L.bga_suffix_reorder.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, P]
     L.bga_beam_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32]
@@ -69,7 +70,7 @@ def load_library(path: str = LIB_PATH):
     L.bga_last_violations.restype = ctypes.c_uint32
     for f in (L.bga_packed_gqa_prefill, L.bga_shared_prefix_decode, L.bga_shared_prefix_decode_packed,
               L.bga_last_token_gather, L.bga_suffix_reorder, L.bga_beam_topk, L.bga_beam_advance,
-              L.bga_suffix_append, L.bga_beam_finalize,
+              L.bga_suffix_append, L.bga_beam_finalize, L.bga_swiglu_quant_e4m3,
               L.bga_beam_topk_noalloc, L.bga_last_hip_error, L.bga_version, L.bga_debug_build):
         f.restype = i32
     return L
@@ -399,3 +400,23 @@ def beam_finalize(pool: dict, cum, tokens, length: int, out: dict | None = None)
                                _ptr(out["lengths"]), _ptr(out["tokens"]), _ptr(out["count"]), _stream(cum))
     _check(st, "bga_beam_finalize")
     return out
+
+
+def swiglu_quant_e4m3(gate_up, codes=None, scale=None):
+    """Fused SwiGLU + per-token E4M3 requantisation. gate_up [T, 2I] bf16 (gate | up).
+    Returns (codes [T, I] uint8 E4M3, scale [T] fp32) with h ~= decode(code) * scale."""
+    _need(gate_up, "gate_up", torch.bfloat16, ndim=2)
+    dev = gate_up.device
+    t, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up must be [T, 2I]")
+    i = two_i // 2
+    if codes is None:
+        codes = torch.empty((t, i), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev, shape=(t, i))
+    if scale is None:
+        scale = torch.empty((t,), dtype=torch.float32, device=dev)
+    _need(scale, "scale", torch.float32, dev, shape=(t,))
+    st = lib.bga_swiglu_quant_e4m3(_ptr(gate_up), t, i, _ptr(codes), _ptr(scale), _stream(gate_up))
+    _check(st, "bga_swiglu_quant_e4m3")
+    return codes, scale

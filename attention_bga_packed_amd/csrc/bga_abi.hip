@@ -397,6 +397,21 @@ bga_status bga_beam_finalize(const float *pool_scores, const int32_t *pool_lengt
                                                 final_lengths, final_tokens, final_count, stream));
 }
 
+bga_status bga_swiglu_quant_e4m3(const bga_bf16 *gate_up, int32_t num_tokens, int32_t inter_size, uint8_t *codes,
+                                 float *scale, hipStream_t stream)
+{
+    if (num_tokens < 0 || inter_size < 8 || inter_size % 8) return BGA_ERR_SHAPE;
+    if (inter_size > bga::swiglu_quant_max_inter()) return BGA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return BGA_OK;
+    if (!gate_up || !codes || !scale) return BGA_ERR_NULL;
+    if (!aligned(gate_up, 16) || !aligned(codes, 8) || !aligned(scale, 4)) return BGA_ERR_ALIGN;
+    const size_t in = (size_t)num_tokens * inter_size * 4, cb = (size_t)num_tokens * inter_size;
+    if (overlap(codes, cb, gate_up, in) || overlap(scale, (size_t)num_tokens * 4, gate_up, in) ||
+        overlap(scale, (size_t)num_tokens * 4, codes, cb))
+        return BGA_ERR_ALIAS;
+    return hip_status(bga::launch_swiglu_quant(gate_up, num_tokens, inter_size, codes, scale, stream));
+}
+
 const char *bga_status_string(bga_status s)
 {
     switch (s) {

@@ -59,6 +59,11 @@ hipError_t launch_beam_finalize(const float *pool_score, const int32_t *pool_len
                                 int W, int len, int tok_cap, float *final_score, int32_t *final_len,
                                 int32_t *final_tok, int32_t *final_count, hipStream_t stream);
 
+// Fused SwiGLU requantisation (swiglu_fp8.hip); I % 8 == 0, I <= swiglu_quant_max_inter().
+int swiglu_quant_max_inter();
+hipError_t launch_swiglu_quant(const uint16_t *gate_up, int T, int I, uint8_t *codes, float *scale,
+                               hipStream_t stream);
+
 #ifdef BGA_DEBUG
 // Debug build: device-side precondition checks (debug_checks.hip). Each runs a
 // check kernel on `stream`, waits for it and returns the BGA_VIOLATION_* bits

@@ -324,6 +324,26 @@ bga_status bga_beam_topk_noalloc(const bga_bf16 *logits, const float *cum_scores
                                  int32_t *out_tokens, int32_t *out_parents, float *out_scores,
                                  int32_t *local_tokens, float *local_scores, float *row_lse, hipStream_t stream);
 
+/*
+ * Fused SwiGLU requantisation to FP8 E4M3 with a per-token dynamic scale
+ * (article section 3.4: after the FP8 Gate/Up projection, one pass per token
+ * computes SiLU(gate) * up in fp32, the amax reduction, the scale and the E4M3
+ * requantisation the FP8 Down projection reads, without writing a bf16 SwiGLU
+ * intermediate).
+ *
+ *   gate_up [T, 2 * inter_size] bf16: per token, gate in columns
+ *           0 .. inter_size-1, up in inter_size .. 2*inter_size-1
+ *   codes   [T, inter_size] uint8, OCP FP8 E4M3 (e4m3fn) codes of
+ *           h * 448 / amax, h = gate / (1 + e^-gate) * up, amax = max(max |h|,
+ *           1e-12), round to nearest even
+ *   scale   [T] fp32: amax / 448, so that h ~= code * scale
+ * Requires inter_size % 8 == 0 and 8 <= inter_size <= 16384; gate_up 16-byte
+ * aligned, codes 8-byte aligned, scale 4-byte aligned; gate_up finite
+ * (precondition).
+ */
+bga_status bga_swiglu_quant_e4m3(const bga_bf16 *gate_up, int32_t num_tokens, int32_t inter_size, uint8_t *codes,
+                                 float *scale, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *bga_status_string(bga_status s);
 

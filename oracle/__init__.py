@@ -57,6 +57,8 @@ def lib():
         L.oracle_num_threads.argtypes = [i32]
         L.oracle_e4m3_encode.argtypes = [f64]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode_array.argtypes = [P, ctypes.c_int64, P]
+        L.oracle_e4m3_encode_array.restype = i32
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = f64
         L.oracle_swiglu_quant.argtypes = [P, i32, i32, P, P, P, P, i32]
@@ -207,9 +209,11 @@ def beam_topk(logits, cum, k_local, k_global, nthreads: int = 0, row_lse=None):
 
 def e4m3_encode(x) -> np.ndarray:
     """OCP E4M3 codes (uint8) of float64 values: round to nearest even, saturating at 448."""
-    x = np.asarray(x, np.float64)
-    f = lib().oracle_e4m3_encode
-    return np.array([f(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.zeros(x.shape, np.uint8)
+    if lib().oracle_e4m3_encode_array(_p(x), x.size, _p(out)):
+        raise ValueError("oracle_e4m3_encode_array rejected its arguments")
+    return out
 
 
 def e4m3_decode(codes) -> np.ndarray:

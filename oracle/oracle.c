@@ -417,6 +417,14 @@ uint8_t oracle_e4m3_encode(double x)
     return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
 }
 
+/* oracle_e4m3_encode over an array (for the tests) */
+int32_t oracle_e4m3_encode_array(const double *x, int64_t n, uint8_t *out)
+{
+    if (!x || !out || n < 0) return 1;
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+    return 0;
+}
+
 /* value of an E4M3 code (for the tests) */
 double oracle_e4m3_decode(uint8_t c)
 {

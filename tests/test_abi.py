@@ -218,3 +218,16 @@ def test_beam_state_update_errors(m):
     assert fin(ln=0) == 2
     assert fin(pc=8190) == 3            # more than 8192 entries to rank
     assert fin(R=0) == 0
+
+
+def test_swiglu_quant_errors(m):
+    def sq(x=P, T=4, I=64, c=2 * P, s=3 * P):
+        return m.lib.bga_swiglu_quant_e4m3(x, T, I, c, s, None)
+    assert sq(I=60) == 2
+    assert sq(I=0) == 2
+    assert sq(T=-1) == 2
+    assert sq(I=16392) == 3
+    assert sq(c=None) == 1
+    assert sq(c=2 * P + 4) == 4
+    assert sq(c=P + 8) == 6             # codes inside gate_up
+    assert sq(T=0) == 0
