@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--only", choices=["prefill_only", "long_prefill", "long_prefill_1024", "short_decode",
                                        "long_beam"], default=None,
                     help="run (and time) only this workload's launches; for profiling one workload")
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="skip the Torch baselines of the article's relative claims")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size dispatch "
                          "for calibrating the FETCH_SIZE / WRITE_SIZE counters)")
@@ -362,6 +364,8 @@ def main():
     else:
         value, unit = hr["achieved"], hr["unit"]
 
+    comps = None if args.no_comparators else comparator_timings(W, timer, rooflines)
+
     cpu = cpus = None
     if args.cpu_seconds > 0 and args.only is None:
         cpus = cpu_baselines(W, args.cpu_seconds)
@@ -393,8 +397,72 @@ def main():
         "rooflines": rooflines,
         "cpu_baseline": cpu,
         "cpu_baselines": cpus,
+        "comparators": comps,
     }
     print(json.dumps(rec), flush=True)
+
+
+def comparator_timings(W, timer, rooflines):
+    """The article's relative claims restated per kernel on this GPU: explicit Torch prefill (padded; packed
+    block-diagonal for the Prefill-Only request) against the packed prefill kernel, and the per-beam full K/V
+    layout (Torch, and the library's own decode with every beam a request of its own) against shared-prefix
+    decode at the workload's longest suffix. `ratio` = baseline time / kernel time."""
+    import math
+
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import comparators as C
+
+    out = {}
+
+    def timed(fn, n=3):
+        return timer.span_ms([fn], n) / n
+
+    for name in ("prefill_only", "long_prefill", "long_prefill_1024"):
+        if name not in W:
+            continue
+        w = W[name]
+        c, lengths = w["cases"][0], w["lengths"]
+        cu = torch.from_numpy(c.cu_seqlens).to(c.q.device)
+        sc = 1.0 / math.sqrt(c.d)
+        kern = rooflines[name]["avg_launch_us"] / 1e3
+        ms = timed(lambda: C.padded_prefill(c.q, c.k, c.v, lengths, sc))
+        out[f"{name}/padded_torch"] = {"ms": round(ms, 4), "kernel_ms": round(kern, 4), "ratio": round(ms / kern, 2)}
+        if name == "prefill_only":
+            ms = timed(lambda: C.packed_prefill(c.q, c.k, c.v, cu, sc))
+            out[f"{name}/packed_torch"] = {"ms": round(ms, 4), "kernel_ms": round(kern, 4),
+                                           "ratio": round(ms / kern, 2)}
+        torch.cuda.empty_cache()
+    for name in ("short_decode", "long_beam"):
+        if name not in W:
+            continue
+        w, cfg = W[name], W[name]["cfg"]
+        c = w["sets"][0]
+        ls = cfg["steps"]
+        sc = 1.0 / math.sqrt(cfg["d"])
+        kern = rooflines[f"{name}/decode"]["us_per_step"][-1] / 1e3
+        R, Wb = cfg["r"], cfg["w"]
+        build = timed(lambda: C.per_beam_kv(c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, ls))
+        kt, vf = C.per_beam_kv(c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, ls)
+        ms = timed(lambda: C.per_beam_decode(c.q, kt, vf, sc))
+        out[f"{name}/per_beam_torch"] = {"ms": round(ms, 4), "layout_build_ms": round(build, 4),
+                                         "kernel_ms": round(kern, 4), "ratio": round(ms / kern, 2),
+                                         "suffix_len": ls}
+        del kt, vf
+        pk, pv = C.per_beam_kv_packed(c.prefix_k, c.prefix_v, c.suffix_k, c.suffix_v, ls)
+        n = cfg["lp"] + ls
+        pcu = torch.arange(0, (R * Wb + 1) * n, n, dtype=torch.int32, device=c.q.device)
+        qb = c.q.reshape(R * Wb, 1, *c.q.shape[2:])
+        dummy = torch.zeros((R * Wb, 1, 1, cfg["nkv"], cfg["d"]), dtype=torch.bfloat16, device=c.q.device)
+        o = torch.empty_like(qb)
+        ms = timed(lambda: bga.shared_prefix_decode_packed(qb, pk, pv, pcu, dummy, dummy, 0, out=o, want_lse=False),
+                   n=5)
+        out[f"{name}/per_beam_own_kernel"] = {"ms": round(ms, 4), "kernel_ms": round(kern, 4),
+                                              "ratio": round(ms / kern, 2), "suffix_len": ls}
+        del pk, pv
+        torch.cuda.empty_cache()
+    return out
 
 
 def workload_config(w):
