@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=1.0,
                     help="scale of the oracle baselines (0 disables them; 1 = the default samples, ~15 s)")
     ap.add_argument("--only", choices=["prefill_only", "long_prefill", "long_prefill_1024", "short_decode",
-                                       "long_beam"], default=None,
+                                       "long_beam", "swiglu_fp8", "long_beam_loop"], default=None,
                     help="run (and time) only this workload's launches; for profiling one workload")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the Torch baselines of the article's relative claims")
@@ -140,7 +140,9 @@ def build_inputs(dev, only=None):
                        ("long_prefill", lambda: prefill_workload("long_prefill", 3, dev)),
                        ("long_prefill_1024", lambda: prefill_workload("long_prefill_1024", 2, dev)),
                        ("short_decode", lambda: short_decode_workload(dev)),
-                       ("long_beam", lambda: long_beam_workload(dev))):
+                       ("long_beam", lambda: long_beam_workload(dev)),
+                       ("swiglu_fp8", lambda: swiglu_workload(dev)),
+                       ("long_beam_loop", lambda: beam_loop_workload(dev))):
         if only is None or only == name:
             W[name] = make()
     return W
@@ -164,8 +166,14 @@ def prefill_workload(name, nsets, dev):
     lse = torch.empty(cases[0].q.shape[:2], dtype=torch.float32, device=dev)
     mx = max(lengths)
     fns = [lambda c=c: bga.packed_gqa_prefill(c.q, c.k, c.v, cu, mx, out=out, lse=lse) for c in cases]
-    return dict(kind="prefill", cfg=cfg, lengths=lengths, cases=cases, fns=fns,
-                step_launches=fns if name == "prefill_only" else fns[:1])
+    w = dict(kind="prefill", cfg=cfg, lengths=lengths, cases=cases, fns=fns,
+             step_launches=fns if name == "prefill_only" else fns[:1])
+    if name == "prefill_only":
+        # the request's output rows at each sequence's last token (the input of the per-sample head)
+        last = torch.empty((len(lengths),) + tuple(out.shape[1:]), dtype=out.dtype, device=dev)
+        w["gather"] = lambda: bga.last_token_gather(out, cu, out=last)
+        w["step_launches"] = fns + [w["gather"]]
+    return w
 
 
 def short_decode_workload(dev):
@@ -245,6 +253,69 @@ def long_beam_workload(dev):
     return dict(kind="beam", cfg=cfg, sets=sets, step=step, decode=dec, reorder=reo, topk=top, logits=logits)
 
 
+def swiglu_workload(dev):
+    """The fused SwiGLU + E4M3 requantisation over the Prefill-Only request's tokens; five input sets (87 MB of
+    traffic each) rotated when timed."""
+    import torch
+
+    import attention_bga_packed_amd as bga
+    import workloads as wl
+
+    cfg = wl.CONFIGS["swiglu_fp8"]
+    t, i = cfg["tokens"], cfg["inter"]
+    sets = []
+    for k in range(5):
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg["seed"] * 1000 + k)
+        sets.append(wl.bf16_normal((t, 2 * i), g, dev, cfg["std"]))
+    codes = torch.empty((t, i), dtype=torch.uint8, device=dev)
+    scale = torch.empty((t,), dtype=torch.float32, device=dev)
+    fns = [lambda x=x: bga.swiglu_quant_e4m3(x, codes=codes, scale=scale) for x in sets]
+    return dict(kind="swiglu", cfg=cfg, fns=fns, step_launches=fns[:1])
+
+
+def beam_loop_workload(dev):
+    """The whole fixed-depth beam search of the long-prompt configuration (8 requests x 400 beams, 480-token
+    prompts, vocabulary 151936): first-step selection, then 5 steps of [suffix append -> shared-prefix decode
+    -> top-K (2W / 2W) -> stop-token split -> reorder], then the final ranking. The model's outputs (query, the
+    current token's K/V, logits N(0, 3)) are synthetic and resident; token 2 stops a hypothesis."""
+    import torch
+
+    import workloads as wl
+    from attention_bga_packed_amd.beam_search import BeamSearch
+
+    cfg = wl.CONFIGS["long_beam"]
+    R, Wb, LP, NS, NQ, NKV, D, V = (cfg[k] for k in ("r", "w", "lp", "steps", "nq", "nkv", "d", "vocab"))
+    n_gen = NS + 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg["seed"] * 31)
+    pk = wl.bf16_normal((R * LP, NKV, D), g, dev)
+    pv = wl.bf16_normal((R * LP, NKV, D), g, dev)
+    pcu = torch.arange(0, (R + 1) * LP, LP, dtype=torch.int32, device=dev)
+    model = {0: {"logits": wl.bf16_normal((R, 1, V), g, dev, cfg["logit_std"])}}
+    for s in range(1, n_gen):
+        model[s] = {"q": wl.bf16_normal((R, Wb, NQ, D), g, dev), "k": wl.bf16_normal((R, Wb, NKV, D), g, dev),
+                    "v": wl.bf16_normal((R, Wb, NKV, D), g, dev),
+                    "logits": wl.bf16_normal((R, Wb, V), g, dev, cfg["logit_std"])}
+    bs = BeamSearch(R, Wb, n_gen, V, NQ, NKV, D, 2, dev)
+
+    def loop():
+        bs.start(pk, pv, pcu, model[0]["logits"])
+        for s in range(1, n_gen):
+            m = model[s]
+            bs.decode(m["q"], m["k"], m["v"])
+            bs.select(m["logits"])
+        bs.finish()
+
+    # algorithmic bytes of one loop: the kernels' own counts summed
+    b = wl.topk_bytes(R, 1, V, 2 * Wb) + wl.beam_advance_bytes(R, Wb, 1, 0)
+    for s in range(1, n_gen):
+        b += wl.suffix_append_bytes(R, Wb, NKV, D) + wl.decode_bytes(R, Wb, NQ, NKV, LP, s, D)
+        b += wl.topk_bytes(R, Wb, V, 2 * Wb) + wl.beam_advance_bytes(R, Wb, Wb, s)
+        b += wl.reorder_bytes(R, Wb, s, NKV, D)
+    return dict(kind="loop", cfg=cfg, fns=[loop], step_launches=[loop], bytes=b, n_gen=n_gen, bs=bs)
+
+
 def roof(bound, achieved, peak, unit, per_launch, ms, traffic):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic, "algorithmic_per_launch": per_launch,
@@ -296,7 +367,7 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        for name in ("prefill_only", "long_prefill", "long_prefill_1024"):
+        for name in ("prefill_only", "long_prefill", "long_prefill_1024", "swiglu_fp8", "long_beam_loop"):
             if name in W:
                 for fn in W[name]["step_launches"]:
                     fn()
@@ -326,6 +397,31 @@ def main():
         n = len(w["fns"]) * max(1, K // len(w["fns"])) if name == "prefill_only" else max(K, 2 * len(w["fns"]))
         ms = timer.span_ms(w["fns"], n) / n
         rooflines[name] = prefill_roofline(name, w, ms)
+    if "prefill_only" in W:
+        w, cfg = W["prefill_only"], W["prefill_only"]["cfg"]
+        n = max(K, 8)
+        ms = timer.span_ms([w["gather"]], n) / n
+        b = wl.gather_bytes(len(w["lengths"]), cfg["nq"] * cfg["d"] * 2)
+        r = roof("hbm", b / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", b, ms, None)
+        r.update({"kernel": "last_token_gather_kernel", "note": "15 rows of 4 KB: bound by launch latency"})
+        rooflines["prefill_only/last_token_gather"] = r
+    if "swiglu_fp8" in W:
+        w, cfg = W["swiglu_fp8"], W["swiglu_fp8"]["cfg"]
+        n = max(K, 2 * len(w["fns"]))
+        ms = timer.span_ms(w["fns"], n) / n
+        b = wl.swiglu_quant_bytes(cfg["tokens"], cfg["inter"])
+        r = roof("hbm", b / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", b, ms, measured_traffic("swiglu_fp8"))
+        r.update({"kernel": "swiglu_quant_kernel"})
+        rooflines["swiglu_fp8"] = r
+    if "long_beam_loop" in W:
+        w = W["long_beam_loop"]
+        n = max(3, K // 3)
+        ms = timer.span_ms(w["fns"], n) / n
+        r = roof("hbm", w["bytes"] / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", w["bytes"], ms, None)
+        r.update({"kernel": "the whole loop (append, decode, top-K, advance, reorder, finalize)",
+                  "ms_per_loop": round(ms, 4), "generated_tokens": w["n_gen"],
+                  "finished_per_request": [int(x) for x in w["bs"].pool["count"].cpu()]})
+        rooflines["long_beam_loop"] = r
     for name in ("short_decode", "long_beam"):
         if name not in W:
             continue
@@ -385,9 +481,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, N(0,3) logits; no weights)",
         "config": {
-            "workload": ("one pass over every measured workload: Prefill-Only request (28 layers), long packed "
-                         "prefill (120 lognormal), long packed prefill 120 x 1024 (headline), short-prompt beam "
-                         "decode (4 steps), long-prompt beam search (5 steps)") if args.only is None else args.only,
+            "workload": ("one pass over every measured workload: Prefill-Only request (28 layers + last-token "
+                         "gather), long packed prefill (120 lognormal), long packed prefill 120 x 1024 (headline), "
+                         "short-prompt beam decode (4 steps), long-prompt beam search (5 steps), SwiGLU E4M3 "
+                         "requantisation (4228 x 4096), the long-prompt fixed-depth beam loop with the 2W stop rule"
+                         ) if args.only is None else args.only,
             "headline": headline,
             "workloads": {n: workload_config(W[n]) for n in W},
             "global_batch": 120 if args.only is None else None,
@@ -468,6 +566,9 @@ def comparator_timings(W, timer, rooflines):
 def workload_config(w):
     cfg = dict(w["cfg"])
     cfg.pop("seed", None)
+    if w["kind"] == "loop":
+        cfg["generated_tokens"] = w["n_gen"]
+        cfg["stop_token"] = 2
     if w["kind"] == "prefill":
         cfg["total_tokens"] = int(sum(w["lengths"]))
         cfg["max_len"] = int(max(w["lengths"]))
@@ -532,6 +633,12 @@ def cpu_baselines(W, scale):
         flops = wl.prefill_flops(lengths[:n], cfg["nq"], cfg["d"])
         out[name] = rec(flops / secs / 1e12, "TFLOP/s", f"{n} of {len(lengths)} sequences (T={t}, "
                         f"{cfg['nq']}/{cfg['nkv']} heads, d {cfg['d']}), {flops / 1e9:.1f} GFLOP", secs)
+    if "swiglu_fp8" in W:
+        cfg = W["swiglu_fp8"]["cfg"]
+        x = W["swiglu_fp8"]["fns"][0].__defaults__[0].cpu()
+        secs = median_of_3(lambda: oracle.swiglu_quant(x, nthreads=threads))
+        b = wl.swiglu_quant_bytes(cfg["tokens"], cfg["inter"])
+        out["swiglu_fp8"] = rec(b / secs / 1e9, "GB/s", f"the whole {cfg['tokens']} x {cfg['inter']} input", secs)
     for name in ("short_decode", "long_beam"):
         if name not in W:
             continue

@@ -33,4 +33,8 @@ from .counts import (  # noqa: F401
     state_elems_shared_prefix,
     state_elems_per_beam,
     effective_mfu,
+    swiglu_quant_bytes,
+    gather_bytes,
+    beam_advance_bytes,
+    suffix_append_bytes,
 )

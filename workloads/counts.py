@@ -69,3 +69,23 @@ def state_elems_per_beam(lp: int, w: int, ls: int, nkv: int, d: int) -> int:
 def effective_mfu(qps: float, f_bf16: float, p_bf16: float, f_fp8: float = 0.0, p_fp8: float = 1.0) -> float:
     """The article's mixed-precision effective MFU: QPS * (F_bf16/P_bf16 + F_fp8/P_fp8)."""
     return qps * (f_bf16 / p_bf16 + f_fp8 / p_fp8)
+
+
+def swiglu_quant_bytes(t: int, inter: int) -> int:
+    """Gate and up read once (bf16), E4M3 codes and the per-token fp32 scale written once."""
+    return t * 2 * inter * 2 + t * inter + 4 * t
+
+
+def gather_bytes(num_seqs: int, row_bytes: int) -> int:
+    """One row read and one written per sequence, plus the offsets."""
+    return 2 * num_seqs * row_bytes + 4 * (num_seqs + 1)
+
+
+def beam_advance_bytes(r: int, w: int, w_in: int, step: int) -> int:
+    """2W candidates read (token, parent, score); W new beams written (parent, score, step + 1 tokens) after
+    reading their source tokens; the finished pool writes are data dependent and not counted."""
+    return r * (2 * w * 12 + w * (8 + 4 * (step + 1)) + w * 4 * step)
+
+
+def suffix_append_bytes(r: int, w: int, nkv: int, d: int) -> int:
+    return 2 * 2 * r * w * nkv * d * 2

@@ -40,6 +40,9 @@ CONFIGS = {
                          nq=16, nkv=8, d=64, seed=4),
     "long_beam": dict(kind="decode", r=8, lp=480, w=400, steps=5, ls_cap=5,
                       nq=16, nkv=8, d=128, seed=5, vocab=151936, logit_std=3.0),
+    # the selective-FP8 SwiGLU requantisation over the Prefill-Only request's tokens; the pages give no model
+    # dimensions, so the intermediate width is a synthetic 4096
+    "swiglu_fp8": dict(kind="swiglu", tokens=4228, inter=4096, std=2.0, seed=6),
 }
 
 
