@@ -62,6 +62,9 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
     if (head_dim != 64 && head_dim != 128) return BGA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || max_seqlen > BGA_MAX_SEQLEN) return BGA_ERR_UNSUPPORTED;
     if ((int64_t)total_tokens * num_q_heads > 0x7fffffff) return BGA_ERR_UNSUPPORTED;   // output row index
+    if (((int64_t)num_seqs * num_kv_heads + 7) / 8 * 8 * (((int64_t)max_seqlen * (num_q_heads / num_kv_heads) + 127) / 128) >
+        0x7fffffff / 256)
+        return BGA_ERR_UNSUPPORTED;   // workgroups of the 1-D grid
     if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return BGA_ERR_SHAPE;
     if (total_tokens > 0 && (num_seqs == 0 || max_seqlen == 0)) return BGA_ERR_SHAPE;   // rows nobody would write
     if (!cu_seqlens) return BGA_ERR_NULL;
@@ -82,8 +85,9 @@ bga_status bga_packed_gqa_prefill(const bga_bf16 *q, const bga_bf16 *k, const bg
         if (st != BGA_OK) return st;
     }
 #endif
-    return hip_status(bga::launch_packed_prefill(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_q_heads,
-                                                 num_kv_heads, head_dim, softmax_scale, out, lse, stream));
+    return hip_status(bga::launch_packed_prefill(q, k, v, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                                 num_q_heads, num_kv_heads, head_dim, softmax_scale, out, lse,
+                                                 stream));
 }
 
 // Host checks shared by both decode entry points (prompt-specific checks are the caller's).

@@ -11,8 +11,8 @@ namespace bga {
 // Every launcher returns hipSuccess or the launch error.
 
 hipError_t launch_packed_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu,
-                                 int num_seqs, int max_seqlen, int nq, int nkv, int d, float scale, uint16_t *out,
-                                 float *lse, hipStream_t stream);
+                                 int num_seqs, int total_tokens, int max_seqlen, int nq, int nkv, int d, float scale,
+                                 uint16_t *out, float *lse, hipStream_t stream);
 
 // prefix_cu == nullptr: prompts of Lp tokens at [R, Lp, Nkv, D]; else request r's
 // prompt is rows prefix_cu[r] .. prefix_cu[r+1]-1 of a packed [T_p, Nkv, D].

@@ -18,14 +18,17 @@
 // last row's token (it still takes part in the copies and barriers of the
 // later ones) and masks only the tiles that reach past its first row's token.
 //
-// Grid = (pairs rounded up to a multiple of 8, row blocks). Pair = (sequence,
-// kv head). Dispatch order over the row blocks: block 0 (one key tile, the
-// shortest) first, then the rest longest first. When the grid exceeds what the
-// GPU holds at once, the block-0 workgroups finish early and free their slots
-// for the overflow, and the long blocks start at once. Consecutive workgroups
-// are dealt round-robin over the 8 XCDs, so the pair index in x, padded to a
-// multiple of 8, keeps every block of one (sequence, kv head) on one XCD and
-// its L2.
+// Grid: (pairs rounded up to a multiple of 8) x (row blocks) workgroups in one
+// dimension. Pair = (sequence, kv head). Consecutive workgroups are dealt
+// round-robin over the 8 XCDs. Block-major order (the default): all pairs'
+// row block 0 (one key tile, the shortest) first, then the other blocks
+// longest first; when the grid exceeds what the GPU holds at once, the block-0
+// workgroups finish early and free their slots for the overflow, and the long
+// blocks start at once; the pair index, padded to a multiple of 8, keeps every
+// block of one (sequence, kv head) on one XCD and its L2. Pair-major order
+// (large batches of equal lengths): each XCD takes its pairs one after another,
+// all blocks of a pair together, longest first, so the K/V it is reading stays
+// in its L2.
 #include "attn_core.hpp"
 #include "internal.hpp"
 
@@ -36,22 +39,36 @@ using namespace core;
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void packed_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ cu, int num_pairs, int blocks_y, int nq, int nkv, int group, float scale,
-    uint16_t *__restrict__ out, float *__restrict__ lse)
+    const int32_t *__restrict__ cu, int num_pairs, int blocks_y, bool pair_major, int nq, int nkv, int group,
+    float scale, uint16_t *__restrict__ out, float *__restrict__ lse)
 {
     using G = Geo<D>;
     constexpr int ROWS = 32 * NW;
     extern __shared__ __align__(16) uint16_t smem[];
 
-    const int pair = group_id_x();
-    if (pair >= num_pairs) return;
     auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    int pair, blk;
+    if (pair_major) {
+        // XCD-aware order for grids much larger than the GPU holds at once: workgroup i runs on XCD i % 8;
+        // the j-th workgroup of XCD x takes pair x + 8 (j / blocks_y), row blocks longest first, so each XCD
+        // works through its pairs one or two at a time and their K/V stays in its L2
+        const int id = group_id_x();
+        const int xcd = id & 7, j = id >> 3;
+        const int jp = uni(j / blocks_y);
+        pair = xcd + 8 * jp;
+        blk = blocks_y - 1 - (j - jp * blocks_y);
+    } else {
+        const int xdim = (num_pairs + 7) / 8 * 8;
+        const int id = group_id_x();
+        const int y = uni(id / xdim);
+        pair = id - y * xdim;
+        // row block of this workgroup: y = 0 -> block 0, y = 1 .. -> blocks_y - 1 down to 1
+        blk = y == 0 ? 0 : blocks_y - y;
+    }
+    if (pair >= num_pairs) return;
     const int seq = uni(pair / nkv), g = pair - seq * nkv;
     const int s0 = cu[seq];
     const int nrows = (cu[seq + 1] - s0) * group;
-    // row block of this workgroup: y = 0 -> block 0, y = 1 .. -> blocks_y - 1 down to 1
-    const int y = group_id_y();
-    const int blk = y == 0 ? 0 : blocks_y - y;
     const int n0 = blk * ROWS;
     if (n0 >= nrows) return;   // uniform over the workgroup
 
@@ -98,8 +115,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
 
 template <int D, int NW>
 static hipError_t launch_prefill_d(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu,
-                                   int num_seqs, int max_seqlen, int nq, int nkv, float scale, uint16_t *out,
-                                   float *lse, hipStream_t stream)
+                                   int num_seqs, int total_tokens, int max_seqlen, int nq, int nkv, float scale,
+                                   uint16_t *out, float *lse, hipStream_t stream)
 {
     const int group = nq / nkv;
     const int pairs = num_seqs * nkv;
@@ -109,18 +126,26 @@ static hipError_t launch_prefill_d(const uint16_t *q, const uint16_t *k, const u
     const void *kern = (const void *)packed_prefill_kernel<D, NW>;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    dim3 grid(xdim, blocks_y), block(64 * NW);
-    hipLaunchKernelGGL((packed_prefill_kernel<D, NW>), grid, block, smem, stream, q, k, v, cu, pairs, blocks_y, nq,
-                       nkv, group, scale, out, lse);
+    // Pair-major order for grids several times what the GPU holds at once whose sequences are (nearly) all
+    // of the longest length: every pair's blocks are then alike and each XCD's L2 keeps its current pairs'
+    // K/V. With lengths that vary, the block-major order spreads the long pairs' work over all XCDs instead
+    // (pair-major measured 3-4 % slower on a lognormal batch, 3 % faster on equal lengths).
+    const bool pair_major = (int64_t)xdim * blocks_y >= 4096 && (int64_t)total_tokens * 10 >= (int64_t)num_seqs * max_seqlen * 9;
+    dim3 grid(xdim * blocks_y), block(64 * NW);
+    hipLaunchKernelGGL((packed_prefill_kernel<D, NW>), grid, block, smem, stream, q, k, v, cu, pairs, blocks_y,
+                       pair_major, nq, nkv, group, scale, out, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_packed_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu,
-                                 int num_seqs, int max_seqlen, int nq, int nkv, int d, float scale, uint16_t *out,
-                                 float *lse, hipStream_t stream)
+                                 int num_seqs, int total_tokens, int max_seqlen, int nq, int nkv, int d, float scale,
+                                 uint16_t *out, float *lse, hipStream_t stream)
 {
-    if (d == 64) return launch_prefill_d<64, 4>(q, k, v, cu, num_seqs, max_seqlen, nq, nkv, scale, out, lse, stream);
-    return launch_prefill_d<128, 4>(q, k, v, cu, num_seqs, max_seqlen, nq, nkv, scale, out, lse, stream);
+    if (d == 64)
+        return launch_prefill_d<64, 4>(q, k, v, cu, num_seqs, total_tokens, max_seqlen, nq, nkv, scale, out, lse,
+                                       stream);
+    return launch_prefill_d<128, 4>(q, k, v, cu, num_seqs, total_tokens, max_seqlen, nq, nkv, scale, out, lse,
+                                    stream);
 }
 
 }  // namespace bga
