@@ -57,9 +57,9 @@ constexpr int TK1_WAVES = TK1_THREADS / 64;
 constexpr int TK1_UNROLL = 4;      // 16-byte chunks in flight per thread
 constexpr int TK_LIST = 4096;      // candidate list entries
 constexpr int TK_SAMPLE = 512;     // sampled 8-logit chunks (4096 logits)
-constexpr int TK_WCAND = 768;      // per wave: candidate entries found in the stream
 constexpr int TK_RING = 128;       // per wave: queued 16-byte chunks holding a candidate
-static_assert(TK1_WAVES * (TK_WCAND + 2 * TK_RING) <= TK_LIST, "candidate regions and rings share the list");
+constexpr int TK_CAP = TK_LIST - TK1_WAVES * 2 * TK_RING;   // candidates the stream can list (3072)
+static_assert(TK_CAP % TK1_THREADS == 0 && TK_CAP >= 2048, "the stream's candidates and the rings share the list");
 constexpr int TK2_THREADS = 1024;  // stage 2: one workgroup per request, one beam per thread
 
 __device__ __forceinline__ uint32_t key16(uint32_t b)
@@ -362,6 +362,30 @@ __device__ __forceinline__ uint32_t sample_select(Tk1Shared &sh, int n, uint32_t
     return prefix;
 }
 
+// The j-th largest (1 <= j <= 128) of the wave's 128 16-bit values (a and b of
+// every lane), four bits per round: candidate d (1..15) extends the prefix by
+// d, two ballots count the values at or above it, and since that count falls
+// as d grows, the number of candidates whose count reaches j is the largest
+// such d. The prefix stays the largest value with at least j values at or
+// above it. Scalar work only after the compares; no LDS, no barrier.
+__device__ __forceinline__ uint32_t wave_jth_largest16(uint32_t a, uint32_t b, uint32_t j)
+{
+    uint32_t prefix = 0;
+#pragma unroll
+    for (int round = 0; round < 4; ++round) {
+        const int shift = 12 - 4 * round;
+        uint32_t d = 0;
+#pragma unroll
+        for (int c = 1; c < 16; ++c) {
+            const uint32_t cand = prefix | ((uint32_t)c << shift);
+            const uint32_t n = (uint32_t)__popcll(__ballot(a >= cand)) + (uint32_t)__popcll(__ballot(b >= cand));
+            d += n >= j ? 1u : 0u;
+        }
+        prefix |= d << shift;
+    }
+    return prefix;
+}
+
 // Raw bf16 bits of row chunk c (8 logits, ids 8c .. 8c+7) as four packed pairs;
 // logits beyond the row read as -inf (0xff80). The load itself is clamped to
 // the row and never skipped, so that a wave's loads are issued unconditionally
@@ -417,22 +441,68 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     const int nrows = (nchunks + TK1_THREADS - 1) / TK1_THREADS;   // chunk rows, id order
     const uint32_t k = (uint32_t)k_local;
 
-    // the stream's first chunks go out now: they land while the threshold is chosen
-    u32x4 bufa[TK1_UNROLL], bufb[TK1_UNROLL];
-#pragma unroll
-    for (int u = 0; u < TK1_UNROLL; ++u) bufa[u] = load_raw<VEC>(x, u * TK1_THREADS + tid, V, nchunks);
-
     // ---- threshold key t from a strided sample (t = 1: every element)
+    // Whole 8-chunk (128-byte) groups spread evenly over the row: the sample
+    // costs its own size in traffic, not one cache line per chunk.
+    const int ns = min(nchunks, TK_SAMPLE);
+    const int ngrp = nchunks >> 3, sgrp = ns >> 3;
+    const int nsamp = ns * 8;
+    // expected count of row keys >= the j-th largest sample key: about j * V / nsamp = 1.5k
+    // (plus a margin of 8 sample ranks)
+    // (32-bit arithmetic: V <= BGA_MAX_VOCAB and k <= BGA_MAX_K keep every product below 2^31)
+    const uint32_t j = min((uint32_t)nsamp, (3u * k * (uint32_t)nsamp + 2u * (uint32_t)V - 1u) / (2u * (uint32_t)V) + 8u);
+    auto sample_chunk = [&](int i) {
+        const uint32_t g = (uint32_t)(i >> 3);
+        const int c = sgrp > 0 && (int)g < sgrp ? (int)((g * (uint32_t)ngrp) / (uint32_t)sgrp) * 8 + (i & 7)
+                                                : (int)(((uint32_t)i * (uint32_t)nchunks) / (uint32_t)ns);
+        return load_keys<VEC>(x, c, V, nchunks);
+    };
+    // the usual sample: 64 groups (sgrp = 64), a shift instead of a division;
+    // raw bits (the index is clamped into the row)
+    auto sample_raw64 = [&](int i) {
+        const int c = min((int)(((uint32_t)(i >> 3) * (uint32_t)ngrp) >> 6) * 8 + (i & 7), nchunks - 1);
+        if (VEC) return *(const u32x4 *)(x + (size_t)c * 8);
+        return load_raw<VEC>(x, c, V, nchunks);   // ids past the row read as -inf, a key below every logit's
+    };
+    // Few sample ranks (the usual case): every wave takes the ceil(j/4)-th
+    // largest of its lanes' two largest sample keys (16 per lane; three of a
+    // wave's top keys rarely share a lane), and t is the mean of the four. The
+    // sample loads go out first, then the stream's first chunks, which land
+    // while the threshold is chosen.
+    const bool quick = V > TK_LIST && j <= 64u && ns == 2 * TK1_THREADS;
+    u32x4 bufa[TK1_UNROLL], bufb[TK1_UNROLL];
+    auto first_batch = [&]() {
+#pragma unroll
+        for (int u = 0; u < TK1_UNROLL; ++u) bufa[u] = load_raw<VEC>(x, u * TK1_THREADS + tid, V, nchunks);
+    };
     uint32_t tkey = 1u;
-    if (V > TK_LIST) {
-        // whole 8-chunk (128-byte) groups spread evenly over the row: the sample
-        // costs its own size in traffic, not one cache line per chunk
-        const int ns = min(nchunks, TK_SAMPLE);
-        const int ngrp = nchunks >> 3, sgrp = ns >> 3;
+    if (quick) {
+        u32x4 smp[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) smp[h] = sample_raw64(h * TK1_THREADS + tid);
+        first_batch();
+        uint32_t k1 = 0u, k2 = 0u;   // the lane's two largest sample keys
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t key = key16((smp[h][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                k2 = max(k2, min(k1, key));
+                k1 = max(k1, key);
+            }
+        const uint32_t tw = wave_jth_largest16(k1, k2, (j + TK1_WAVES - 1) / TK1_WAVES);
+        if (lane == 0) sh.wcnt[w] = tw;
+        __syncthreads();
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < TK1_WAVES; ++i) sum += sh.wcnt[i];
+        tkey = sum / TK1_WAVES;
+    } else {
+        first_batch();
+    }
+    if (!quick && V > TK_LIST) {
         for (int i = tid; i < ns; i += TK1_THREADS) {
-            const int c = sgrp > 0 && (i >> 3) < sgrp ? (int)(((long long)(i >> 3) * ngrp) / sgrp) * 8 + (i & 7)
-                                                      : (int)(((long long)i * nchunks) / ns);
-            const u32x4 kk = load_keys<VEC>(x, c, V, nchunks);
+            const u32x4 kk = sample_chunk(i);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 sh.sample[i * 8 + 2 * e] = (uint16_t)(kk[e] & 0xffffu);
@@ -440,28 +510,23 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             }
         }
         __syncthreads();
-        const int nsamp = ns * 8;
-        // expected count of row keys >= the j-th largest sample key: about j * V / nsamp = 1.5k
-        // (plus a margin of 8 sample ranks)
-        const uint32_t j = (uint32_t)min((long long)nsamp, (3ll * k * nsamp + 2ll * V - 1) / (2ll * V) + 8);
         tkey = sample_select(sh, nsamp, j);
-        __syncthreads();   // the sample is dead: the list reuses its memory
     }
+    if (tid == 0) sh.count = 0;
+    __syncthreads();   // the sample and the threshold's words are dead: the list reuses that memory
     const float tval = tkey > 1u ? key16_value(tkey) : -INFINITY;   // value form of the cut (prefilter)
-    __syncthreads();
 
     // ---- stream: per-lane lazy offset m and fp64 sum of exp(x - m); candidates >= t
     // A chunk whose maximum reaches t is pushed (data and index) onto the wave's
     // ring in LDS; whenever 64 are queued the wave takes one per lane, extracts
-    // its keys >= t and appends them to the wave's candidate region. The row is
-    // read once: the candidates come from data already in registers.
+    // its keys >= t and appends them to the block's candidate list (one LDS
+    // atomic per wave reserves the places). The row is read once: the
+    // candidates come from data already in registers.
     float m = -INFINITY;
     double acc = 0.0;
     uint32_t rpos = 0;     // ring fill (wave-uniform)
-    uint32_t lcount = 0;   // candidates this wave found (wave-uniform; stored while < TK_WCAND)
-    u32x4 *const ring = (u32x4 *)(sh.list + TK1_WAVES * TK_WCAND) + w * TK_RING;
+    u32x4 *const ring = (u32x4 *)(sh.list + TK_CAP) + w * TK_RING;
     uint32_t *const ring_id = &sh.whist[0][0] + w * TK_RING;
-    unsigned long long *const wlist = sh.list + w * TK_WCAND;
     auto drain = [&](uint32_t n) {   // the ring's first n <= 64 chunks (wave-uniform n)
         const bool have = (uint32_t)lane < n;
         const u32x4 d = have ? ring[lane] : u32x4{0u, 0u, 0u, 0u};
@@ -478,17 +543,18 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         const uint32_t cnt = (uint32_t)__popc(hm);
         const uint32_t incl = wave_incl_scan_u32(cnt);
         const uint32_t tot = (uint32_t)__shfl(incl, 63);
-        uint32_t at = lcount + incl - cnt;
+        uint32_t base = 0;
+        if (lane == 0 && tot) base = atomicAdd(&sh.count, tot);   // past TK_CAP: counted, not stored
+        uint32_t at = (uint32_t)__shfl((int)base, 0) + incl - cnt;
         while (hm) {
             const int b = __ffs(hm) - 1;
             hm &= hm - 1;
             const uint32_t word = d[b >> 1];
             const uint32_t key = key16((b & 1) ? (word >> 16) : (word & 0xffffu));
             const uint32_t id = (uint32_t)(c * 8 + b);
-            if (at < (uint32_t)TK_WCAND) wlist[at] = ((unsigned long long)key << 32) | (0xffffffffu - id);
+            if (at < (uint32_t)TK_CAP) sh.list[at] = ((unsigned long long)key << 32) | (0xffffffffu - id);
             ++at;
         }
-        lcount += tot;
         // move the rest of the ring down (same wave: LDS keeps this order)
         const uint32_t rest = rpos - n;
         if ((uint32_t)lane < rest) {
@@ -556,46 +622,14 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     }
     while (rpos > 0u) drain(min(rpos, 64u));
 
-    // ---- candidates: the waves' regions, compacted into one list
-    if (lane == 0) sh.wcnt[w] = lcount;
+    // ---- candidates: list[0, count) (every key >= t if the list held them all)
     __syncthreads();
-    uint32_t wc[TK1_WAVES], count = 0;
-    bool noted_all = true;
-#pragma unroll
-    for (int i = 0; i < TK1_WAVES; ++i) {
-        wc[i] = sh.wcnt[i];
-        noted_all = noted_all && wc[i] <= (uint32_t)TK_WCAND;
-        wc[i] = min(wc[i], (uint32_t)TK_WCAND);
-        count += wc[i];
-    }
+    const uint32_t found = sh.count;
+    const bool noted_all = found <= (uint32_t)TK_CAP;
+    const uint32_t count = min(found, (uint32_t)TK_CAP);
     // the same value in every thread: kept in a scalar register, so that the
     // loops below skip whole iterations past the listed entries
     const int ucnt = __builtin_amdgcn_readfirstlane((int)count);
-    {
-        constexpr int kPer = TK1_WAVES * TK_WCAND / TK1_THREADS;
-        unsigned long long e[kPer];
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            e[j] = 0ull;
-            if (j * TK1_THREADS >= ucnt) continue;
-            // flat index f over the waves' regions -> (wave, slot)
-            uint32_t f = (uint32_t)(tid + j * TK1_THREADS), src = 0xffffffffu;
-#pragma unroll
-            for (int i = 0; i < TK1_WAVES; ++i) {
-                if (src == 0xffffffffu && f < wc[i]) src = (uint32_t)(i * TK_WCAND) + f;
-                f = f >= wc[i] ? f - wc[i] : 0xffffffffu;
-            }
-            e[j] = src != 0xffffffffu ? sh.list[src] : 0ull;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const uint32_t f = (uint32_t)(tid + j * TK1_THREADS);
-            if (j * TK1_THREADS < ucnt && f < count) sh.list[f] = e[j];
-        }
-    }
-    if (tid == 0) sh.count = count;
-    __syncthreads();
 
     // ---- the row's log-sum-exp from the lanes' (m, sum)
     float M = m;
@@ -628,11 +662,11 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     // ---- the cut key kappa, keys above it, keys equal to it
     uint32_t kappa, above, n_eq;
     int n;
-    if (noted_all && count >= k && count <= (uint32_t)TK_LIST) {
+    if (noted_all && count >= k) {
         // Common case: a counting sort by key offset from t. Every listed key
         // is >= t; when they span < 1024 values, bins give each key's place
         // (keys above it) and ranks by id inside a bin finish the order.
-        constexpr int kPerT = TK_LIST / TK1_THREADS;
+        constexpr int kPerT = TK_CAP / TK1_THREADS;
         unsigned long long ent[kPerT];
         bool wide = false;
 #pragma unroll
@@ -646,7 +680,8 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         if (!__syncthreads_or(wide)) {
             uint32_t *hist = &sh.whist[0][0];                     // 1024 bins
             uint32_t *start = (uint32_t *)sh.list;                 // keys above each bin
-            unsigned long long *bkt = sh.list + 512;               // selected entries, bin by bin
+            uint32_t *bid = (uint32_t *)(sh.list + 512);           // selected entries' ~id, bin by bin
+            uint16_t *sbin = (uint16_t *)(sh.list + 2560);         // the bin of each filled slot
             unsigned long long *out = sh.list + 1536;              // the k chosen, in place order
             for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;
             __syncthreads();
@@ -661,7 +696,6 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
                 hc[q] = hist[1023 - 4 * tid - q];   // thread t: bins 1023-4t down to 1020-4t
                 loc += hc[q];
             }
-            if (tid == 0) sh.c.bcast[1] = 0;
             uint32_t tot;
             uint32_t run = block_excl_scan(sh.c, loc, &tot);   // (the list is in registers: its memory is free)
 #pragma unroll
@@ -673,51 +707,61 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             }
             __syncthreads();
             const uint32_t bk = sh.c.bcast[0];   // bin of the k-th largest key
-            uint32_t hmax = 0;   // largest bin at or above bk: one LDS atomic per wave
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if ((uint32_t)(1023 - 4 * tid - q) >= bk) hmax = max(hmax, hc[q]);
-            hmax = wave_max_u32(hmax);
-            if (lane == 0 && hmax) atomicMax(&sh.c.bcast[1], hmax);
-            __syncthreads();
-            const uint32_t nsel = start[bk] + hist[bk], bmax = sh.c.bcast[1];
-            __syncthreads();   // every thread has read nsel and bmax: the decision is uniform
-            if (nsel <= 1024 && bmax <= 64) {
+            const uint32_t nsel = start[bk] + hist[bk];
+            __syncthreads();   // every thread has read nsel: the decision is uniform
+            if (nsel <= 1024) {
                 for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;   // now: fill cursors
                 __syncthreads();
-                uint32_t pos[kPerT];
 #pragma unroll
                 for (int j = 0; j < kPerT; ++j) {
-                    pos[j] = 0xffffffffu;
                     if (j * TK1_THREADS >= ucnt) continue;
                     const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey;
                     if ((uint32_t)(tid + j * TK1_THREADS) < count && dk >= bk) {
-                        const uint32_t b0 = start[dk];
-                        pos[j] = b0;
-                        bkt[b0 + atomicAdd(&hist[dk], 1u)] = ent[j];
+                        const uint32_t slot = start[dk] + atomicAdd(&hist[dk], 1u);
+                        bid[slot] = (uint32_t)ent[j];
+                        sbin[slot] = (uint16_t)dk;
                     }
                 }
                 __syncthreads();
+                // Every filled slot p (thread t: slots t, t + 256, t + 512, t + 768)
+                // ranks its entry inside its bin: the bin's entries with a lower id
+                // (a larger ~id), eight per pair of 16-byte reads from the aligned
+                // slots around the bin, the four slots' reads issued together.
+                // Slots outside the bin are masked; reads stay below slot 1028.
+                uint32_t b0[4], b1[4], mine[4], rank[4], span = 0;
 #pragma unroll
-                for (int j = 0; j < kPerT; ++j)
-                    if (j * TK1_THREADS < ucnt && pos[j] != 0xffffffffu) {
-                        const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey, nb = hist[dk];
-                        const uint32_t myid = 0xffffffffu - (uint32_t)(ent[j] & 0xffffffffu);
-                        // entries of the bin with a lower id (four reads in flight at a time)
-                        const unsigned long long *bb = bkt + pos[j];
-                        const uint32_t cmp = 0xffffffffu - myid;   // lower id <=> larger low word
-                        uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0, i = 0;
-                        for (; i + 4 <= nb; i += 4) {
-                            r0 += (uint32_t)bb[i] > cmp;
-                            r1 += (uint32_t)bb[i + 1] > cmp;
-                            r2 += (uint32_t)bb[i + 2] > cmp;
-                            r3 += (uint32_t)bb[i + 3] > cmp;
-                        }
-                        for (; i < nb; ++i) r0 += (uint32_t)bb[i] > cmp;
-                        const uint32_t rank = r0 + r1 + r2 + r3;
-                        const uint32_t at = pos[j] + rank;
-                        if (at < (uint32_t)k_local) out[at] = ((unsigned long long)(tkey + dk) << 32) | myid;
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t p = (uint32_t)(tid + q * TK1_THREADS);
+                    b0[q] = b1[q] = mine[q] = rank[q] = 0;
+                    if (p < nsel) {
+                        const uint32_t dk = sbin[p];
+                        b0[q] = start[dk];
+                        b1[q] = b0[q] + hist[dk];
+                        mine[q] = bid[p];
+                        span = max(span, b1[q] - (b0[q] & ~3u));
                     }
+                }
+#pragma unroll 1
+                for (uint32_t off = 0; off < span; off += 8) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t a = (b0[q] & ~3u) + off;
+                        if (a < b1[q]) {
+                            const u32x4 q0 = *(const u32x4 *)(bid + a), q1 = *(const u32x4 *)(bid + a + 4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                rank[q] += (a + e >= b0[q] && a + e < b1[q] && q0[e] > mine[q]) ? 1u : 0u;
+                                rank[q] += (a + 4 + e < b1[q] && q1[e] > mine[q]) ? 1u : 0u;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t p = (uint32_t)(tid + q * TK1_THREADS), at = b0[q] + rank[q];
+                    if (p < nsel && at < (uint32_t)k_local)
+                        out[at] = ((unsigned long long)(tkey + sbin[p]) << 32) | (0xffffffffu - mine[q]);
+                }
                 __syncthreads();
                 // the k entries in place order: consecutive threads store consecutive places
                 for (int j = tid; j < k_local; j += TK1_THREADS) {
@@ -741,9 +785,9 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             for (uint32_t i = tid; i < count; i += TK1_THREADS) fn((uint32_t)(sh.list[i] >> 32));
         }, k, &above, &n_eq);
         // keep the entries >= kappa (order does not matter: they are sorted next)
-        unsigned long long mine[TK_LIST / TK1_THREADS];
+        unsigned long long mine[TK_CAP / TK1_THREADS];
 #pragma unroll
-        for (int i = 0; i < TK_LIST / TK1_THREADS; ++i) {
+        for (int i = 0; i < TK_CAP / TK1_THREADS; ++i) {
             const uint32_t idx = (uint32_t)(tid + i * TK1_THREADS);
             mine[i] = i * TK1_THREADS < ucnt && idx < count ? sh.list[idx] : 0ull;
         }
@@ -751,7 +795,7 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         if (tid == 0) sh.count = 0;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < TK_LIST / TK1_THREADS; ++i)
+        for (int i = 0; i < TK_CAP / TK1_THREADS; ++i)
             if (i * TK1_THREADS < ucnt && (uint32_t)(mine[i] >> 32) >= kappa)
                 sh.list[atomicAdd(&sh.count, 1u)] = mine[i];
         n = (int)(above + n_eq);
