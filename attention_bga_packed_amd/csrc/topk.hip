@@ -58,8 +58,11 @@ constexpr int TK1_UNROLL = 4;      // 16-byte chunks in flight per thread
 constexpr int TK_LIST = 4096;      // candidate list entries
 constexpr int TK_SAMPLE = 512;     // sampled 8-logit chunks (4096 logits)
 constexpr int TK_RING = 128;       // per wave: queued 16-byte chunks holding a candidate
-constexpr int TK_CAP = TK_LIST - TK1_WAVES * 2 * TK_RING;   // candidates the stream can list (3072)
-static_assert(TK_CAP % TK1_THREADS == 0 && TK_CAP >= 2048, "the stream's candidates and the rings share the list");
+constexpr int TK_RING_U64 = TK1_WAVES * 2 * TK_RING;       // the rings' share of the list, at its end
+constexpr int TK_CAP = 2 * (TK_LIST - TK_RING_U64);        // candidates the stream can list (6144 words)
+static_assert(TK_CAP % TK1_THREADS == 0 && TK_CAP >= 4096, "the stream's candidates and the rings share the list");
+// a listed candidate is one word: (key - t) << 18 | (2^18 - 1 - id)
+static_assert(BGA_MAX_VOCAB <= (1 << 18), "token ids fit 18 bits");
 constexpr int TK2_THREADS = 1024;  // stage 2: one workgroup per request, one beam per thread
 
 __device__ __forceinline__ uint32_t key16(uint32_t b)
@@ -327,7 +330,9 @@ struct Tk1Shared {
     float lmax[TK1_THREADS / 64];
     double dsum[TK1_THREADS / 64];
     uint32_t wcnt[TK1_THREADS / 64];
+    uint32_t ring_id[TK1_THREADS / 64][TK_RING];   // chunk index of each queued chunk
     uint32_t count;
+    uint32_t wide;                            // a candidate lies 1024 or more keys above t
 };
 
 // The j-th largest nonzero key of sh.sample[0..n) (two 8-bit digits; each wave
@@ -440,6 +445,7 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     const int nchunks = (V + 7) / 8;
     const int nrows = (nchunks + TK1_THREADS - 1) / TK1_THREADS;   // chunk rows, id order
     const uint32_t k = (uint32_t)k_local;
+    const float c0 = cum ? cum[row] : 0.f;   // (needed at the end; loaded now)
 
     // ---- threshold key t from a strided sample (t = 1: every element)
     // Whole 8-chunk (128-byte) groups spread evenly over the row: the sample
@@ -512,7 +518,13 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         __syncthreads();
         tkey = sample_select(sh, nsamp, j);
     }
-    if (tid == 0) sh.count = 0;
+    // the stream counts its candidates' keys into 1024 bins above t
+    uint32_t *const hist = &sh.whist[0][0];
+    for (int i = tid; i < 1024; i += TK1_THREADS) hist[i] = 0u;
+    if (tid == 0) {
+        sh.count = 0u;
+        sh.wide = 0u;
+    }
     __syncthreads();   // the sample and the threshold's words are dead: the list reuses that memory
     const float tval = tkey > 1u ? key16_value(tkey) : -INFINITY;   // value form of the cut (prefilter)
 
@@ -525,8 +537,9 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     float m = -INFINITY;
     double acc = 0.0;
     uint32_t rpos = 0;     // ring fill (wave-uniform)
-    u32x4 *const ring = (u32x4 *)(sh.list + TK_CAP) + w * TK_RING;
-    uint32_t *const ring_id = &sh.whist[0][0] + w * TK_RING;
+    u32x4 *const ring = (u32x4 *)(sh.list + (TK_LIST - TK_RING_U64)) + w * TK_RING;
+    uint32_t *const list32 = (uint32_t *)sh.list;
+    uint32_t *const ring_id = sh.ring_id[w];
     auto drain = [&](uint32_t n) {   // the ring's first n <= 64 chunks (wave-uniform n)
         const bool have = (uint32_t)lane < n;
         const u32x4 d = have ? ring[lane] : u32x4{0u, 0u, 0u, 0u};
@@ -537,7 +550,8 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             hm |= (bf16_lo(d[e]) >= tval ? 1u : 0u) << (2 * e);
             hm |= (bf16_hi(d[e]) >= tval ? 1u : 0u) << (2 * e + 1);
         }
-        // finite logits: value order is key order. Only chunks inside the row
+        // finite logits: value order is key order (a candidate's key is >= t).
+        // Only chunks inside the row
         // are queued (c < nchunks, so 1 <= V - 8c); its ids >= V are padding.
         hm = have ? hm & ((1u << min(8, V - c * 8)) - 1u) : 0u;
         const uint32_t cnt = (uint32_t)__popc(hm);
@@ -552,7 +566,13 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
             const uint32_t word = d[b >> 1];
             const uint32_t key = key16((b & 1) ? (word >> 16) : (word & 0xffffu));
             const uint32_t id = (uint32_t)(c * 8 + b);
-            if (at < (uint32_t)TK_CAP) sh.list[at] = ((unsigned long long)key << 32) | (0xffffffffu - id);
+            const uint32_t dk = key - tkey;
+            if (dk < 1024u) {
+                atomicAdd(&hist[dk], 1u);
+                if (at < (uint32_t)TK_CAP) list32[at] = (dk << 18) | (0x3ffffu - id);
+            } else {
+                sh.wide = 1u;
+            }
             ++at;
         }
         // move the rest of the ring down (same wave: LDS keeps this order)
@@ -622,7 +642,14 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     }
     while (rpos > 0u) drain(min(rpos, 64u));
 
-    // ---- candidates: list[0, count) (every key >= t if the list held them all)
+    // ---- after the stream: the candidate count, the row's log-sum-exp and (the
+    // usual case) the scan of the bin counts the stream kept, in two barriers
+    {
+        float Mw = m;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, o));
+        if (lane == 0) sh.lmax[w] = Mw;
+    }
     __syncthreads();
     const uint32_t found = sh.count;
     const bool noted_all = found <= (uint32_t)TK_CAP;
@@ -630,25 +657,41 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
     // the same value in every thread: kept in a scalar register, so that the
     // loops below skip whole iterations past the listed entries
     const int ucnt = __builtin_amdgcn_readfirstlane((int)count);
+    float M = sh.lmax[0];
+#pragma unroll
+    for (int i = 1; i < TK1_WAVES; ++i) M = fmaxf(M, sh.lmax[i]);
+    {
+        double part = (m != -INFINITY) ? acc * exp((double)m - (double)M) : 0.0;
+        part = wave_sum_f64(part);
+        if (lane == 0) sh.dsum[w] = part;
+    }
+    // Counting sort by key offset from t when every key >= t is listed, there
+    // are at least k, and all lie within 1024 keys of t: the bins give each
+    // key's place (keys above it) and ranks by id inside a bin finish the order.
+    const bool fast = noted_all && count >= k && sh.wide == 0u;
+    constexpr int kPerT = TK_CAP / TK1_THREADS;
+    uint32_t ent[kPerT];
+    uint32_t hc[4], loc = 0, incl = 0;
+    if (fast) {
+#pragma unroll
+        for (int j = 0; j < kPerT; ++j) {
+            const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
+            ent[j] = (j * TK1_THREADS < ucnt && idx < count) ? list32[idx] : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hc[q] = hist[1023 - 4 * tid - q];   // thread t: bins 1023-4t down to 1020-4t
+            loc += hc[q];
+        }
+        incl = wave_incl_scan_u32(loc);
+        if (lane == 63) sh.c.wsum[w] = incl;
+    }
+    __syncthreads();   // (every listed entry is in registers: the list's memory is free)
+    double dtot = 0.0;
+#pragma unroll
+    for (int i = 0; i < TK1_WAVES; ++i) dtot += sh.dsum[i];
+    const float lse32 = (float)((double)M + log(dtot));
 
-    // ---- the row's log-sum-exp from the lanes' (m, sum)
-    float M = m;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (lane == 0) sh.lmax[w] = M;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TK1_THREADS / 64; ++i) M = fmaxf(M, sh.lmax[i]);
-    double part = (m != -INFINITY) ? acc * exp((double)m - (double)M) : 0.0;
-    part = wave_sum_f64(part);
-    if (lane == 0) sh.dsum[w] = part;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int i = 0; i < TK1_THREADS / 64; ++i) tot += sh.dsum[i];
-    const float lse32 = (float)((double)M + log(tot));
-
-    const float c0 = cum ? cum[row] : 0.f;
     auto emit = [&](int j, uint32_t key, int32_t id) {
         const float lp = key16_value(key) - lse32;
         const float s = c0 + lp;
@@ -659,148 +702,98 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
         if (local_score) local_score[o] = s;
     };
 
-    // ---- the cut key kappa, keys above it, keys equal to it
-    uint32_t kappa, above, n_eq;
-    int n;
-    if (noted_all && count >= k) {
-        // Common case: a counting sort by key offset from t. Every listed key
-        // is >= t; when they span < 1024 values, bins give each key's place
-        // (keys above it) and ranks by id inside a bin finish the order.
-        constexpr int kPerT = TK_CAP / TK1_THREADS;
-        unsigned long long ent[kPerT];
-        bool wide = false;
+    if (fast) {
+        uint32_t *start = list32;                   // entries above each bin (1024)
+        uint32_t *bid = list32 + 1024;              // selected entries' low words, bin by bin (2048 + 8)
+        uint32_t *out = list32 + 3088;              // the k chosen, in place order (<= 1024)
+        uint16_t *sbin = (uint16_t *)(list32 + 4112);   // the bin of each filled slot (2048)
+        uint32_t run = incl - loc;
+        for (int i = 0; i < w; ++i) run += sh.c.wsum[i];
 #pragma unroll
-        for (int j = 0; j < kPerT; ++j) {
-            ent[j] = 0ull;
-            if (j * TK1_THREADS >= ucnt) continue;
-            const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
-            ent[j] = idx < count ? sh.list[idx] : 0ull;
-            wide = wide || (idx < count && (uint32_t)(ent[j] >> 32) - tkey >= 1024u);
+        for (int q = 0; q < 4; ++q) {
+            const int b = 1023 - 4 * tid - q;
+            start[b] = run;
+            if (run < k && run + hc[q] >= k) {
+                sh.c.bcast[0] = (uint32_t)b;
+                sh.c.bcast[1] = run + hc[q];
+            }
+            run += hc[q];
         }
-        if (!__syncthreads_or(wide)) {
-            uint32_t *hist = &sh.whist[0][0];                     // 1024 bins
-            uint32_t *start = (uint32_t *)sh.list;                 // keys above each bin
-            uint32_t *bid = (uint32_t *)(sh.list + 512);           // selected entries' ~id, bin by bin
-            uint16_t *sbin = (uint16_t *)(sh.list + 2560);         // the bin of each filled slot
-            unsigned long long *out = sh.list + 1536;              // the k chosen, in place order
-            for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;
-            __syncthreads();
+        __syncthreads();
+        const uint32_t bk = sh.c.bcast[0];     // bin of the k-th largest key
+        const uint32_t nsel = sh.c.bcast[1];   // entries in bins bk and above
+        if (nsel <= 2048) {
+            // bin dk holds slots [start[dk], start[dk - 1]) (start[-1] = count);
+            // its counter, counted down, hands out the slots
 #pragma unroll
-            for (int j = 0; j < kPerT; ++j)
-                if (j * TK1_THREADS < ucnt && (uint32_t)(tid + j * TK1_THREADS) < count)
-                    atomicAdd(&hist[(uint32_t)(ent[j] >> 32) - tkey], 1u);
-            __syncthreads();
-            uint32_t hc[4], loc = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                hc[q] = hist[1023 - 4 * tid - q];   // thread t: bins 1023-4t down to 1020-4t
-                loc += hc[q];
-            }
-            uint32_t tot;
-            uint32_t run = block_excl_scan(sh.c, loc, &tot);   // (the list is in registers: its memory is free)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int b = 1023 - 4 * tid - q;
-                start[b] = run;
-                if (run < k && run + hc[q] >= k) sh.c.bcast[0] = (uint32_t)b;
-                run += hc[q];
+            for (int j = 0; j < kPerT; ++j) {
+                if (j * TK1_THREADS >= ucnt) continue;
+                const uint32_t dk = ent[j] >> 18;
+                if ((uint32_t)(tid + j * TK1_THREADS) < count && dk >= bk) {
+                    const uint32_t slot = start[dk] + atomicSub(&hist[dk], 1u) - 1u;
+                    bid[slot] = ent[j] & 0x3ffffu;
+                    sbin[slot] = (uint16_t)dk;
+                }
             }
             __syncthreads();
-            const uint32_t bk = sh.c.bcast[0];   // bin of the k-th largest key
-            const uint32_t nsel = start[bk] + hist[bk];
-            __syncthreads();   // every thread has read nsel: the decision is uniform
-            if (nsel <= 1024) {
-                for (int b = tid; b < 1024; b += TK1_THREADS) hist[b] = 0;   // now: fill cursors
-                __syncthreads();
+            // Every filled slot p (thread t: slots t + 256 q, q < 8) ranks its
+            // entry inside its bin: the bin's entries with a lower id (a larger
+            // low word), eight per pair of 16-byte reads from the aligned slots
+            // around the bin, the eight slots' reads issued together. Slots
+            // outside the bin are masked (reads past slot 2047 stay inside the
+            // padding and are masked too).
+            constexpr int NQ = 2048 / TK1_THREADS;
+            uint32_t b0[NQ], b1[NQ], mine[NQ], rank[NQ], span = 0;
 #pragma unroll
-                for (int j = 0; j < kPerT; ++j) {
-                    if (j * TK1_THREADS >= ucnt) continue;
-                    const uint32_t dk = (uint32_t)(ent[j] >> 32) - tkey;
-                    if ((uint32_t)(tid + j * TK1_THREADS) < count && dk >= bk) {
-                        const uint32_t slot = start[dk] + atomicAdd(&hist[dk], 1u);
-                        bid[slot] = (uint32_t)ent[j];
-                        sbin[slot] = (uint16_t)dk;
-                    }
+            for (int q = 0; q < NQ; ++q) {
+                const uint32_t p = (uint32_t)(tid + q * TK1_THREADS);
+                b0[q] = b1[q] = mine[q] = rank[q] = 0;
+                if (p < nsel) {
+                    const uint32_t dk = sbin[p];
+                    b0[q] = start[dk];
+                    b1[q] = dk > 0u ? start[dk - 1] : count;
+                    mine[q] = bid[p];
+                    span = max(span, b1[q] - (b0[q] & ~3u));
                 }
-                __syncthreads();
-                // Every filled slot p (thread t: slots t, t + 256, t + 512, t + 768)
-                // ranks its entry inside its bin: the bin's entries with a lower id
-                // (a larger ~id), eight per pair of 16-byte reads from the aligned
-                // slots around the bin, the four slots' reads issued together.
-                // Slots outside the bin are masked; reads stay below slot 1028.
-                uint32_t b0[4], b1[4], mine[4], rank[4], span = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t p = (uint32_t)(tid + q * TK1_THREADS);
-                    b0[q] = b1[q] = mine[q] = rank[q] = 0;
-                    if (p < nsel) {
-                        const uint32_t dk = sbin[p];
-                        b0[q] = start[dk];
-                        b1[q] = b0[q] + hist[dk];
-                        mine[q] = bid[p];
-                        span = max(span, b1[q] - (b0[q] & ~3u));
-                    }
-                }
+            }
 #pragma unroll 1
-                for (uint32_t off = 0; off < span; off += 8) {
+            for (uint32_t off = 0; off < span; off += 8) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t a = (b0[q] & ~3u) + off;
-                        if (a < b1[q]) {
-                            const u32x4 q0 = *(const u32x4 *)(bid + a), q1 = *(const u32x4 *)(bid + a + 4);
+                for (int q = 0; q < NQ; ++q) {
+                    const uint32_t a = (b0[q] & ~3u) + off;
+                    if (a < b1[q]) {
+                        const u32x4 q0 = *(const u32x4 *)(bid + a), q1 = *(const u32x4 *)(bid + a + 4);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                rank[q] += (a + e >= b0[q] && a + e < b1[q] && q0[e] > mine[q]) ? 1u : 0u;
-                                rank[q] += (a + 4 + e < b1[q] && q1[e] > mine[q]) ? 1u : 0u;
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            rank[q] += (a + e >= b0[q] && a + e < b1[q] && q0[e] > mine[q]) ? 1u : 0u;
+                            rank[q] += (a + 4 + e < b1[q] && q1[e] > mine[q]) ? 1u : 0u;
                         }
                     }
                 }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t p = (uint32_t)(tid + q * TK1_THREADS), at = b0[q] + rank[q];
-                    if (p < nsel && at < (uint32_t)k_local)
-                        out[at] = ((unsigned long long)(tkey + sbin[p]) << 32) | (0xffffffffu - mine[q]);
-                }
-                __syncthreads();
-                // the k entries in place order: consecutive threads store consecutive places
-                for (int j = tid; j < k_local; j += TK1_THREADS) {
-                    const unsigned long long e = out[j];
-                    emit(j, (uint32_t)(e >> 32), (int32_t)(uint32_t)e);
-                }
-                if (tid == 0 && row_lse) row_lse[row] = lse32;
-                return;
             }
-            // put the list back for the general path below
-            __syncthreads();
 #pragma unroll
-            for (int j = 0; j < kPerT; ++j) {
-                const uint32_t idx = (uint32_t)(tid + j * TK1_THREADS);
-                if (j * TK1_THREADS < ucnt && idx < count) sh.list[idx] = ent[j];
+            for (int q = 0; q < NQ; ++q) {
+                const uint32_t p = (uint32_t)(tid + q * TK1_THREADS), at = b0[q] + rank[q];
+                if (p < nsel && at < (uint32_t)k_local) out[at] = ((uint32_t)sbin[p] << 18) | mine[q];
             }
             __syncthreads();
+            // the k entries in place order: consecutive threads store consecutive places
+            for (int j = tid; j < k_local; j += TK1_THREADS) {
+                const uint32_t e = out[j];
+                emit(j, tkey + (e >> 18), (int32_t)(0x3ffffu - (e & 0x3ffffu)));
+            }
+            if (tid == 0 && row_lse) row_lse[row] = lse32;
+            return;
         }
-        // every row key >= t is listed, and the k-th largest is one of them
-        kappa = radix_select<2>(sh.c, [&](auto fn) {
-            for (uint32_t i = tid; i < count; i += TK1_THREADS) fn((uint32_t)(sh.list[i] >> 32));
-        }, k, &above, &n_eq);
-        // keep the entries >= kappa (order does not matter: they are sorted next)
-        unsigned long long mine[TK_CAP / TK1_THREADS];
-#pragma unroll
-        for (int i = 0; i < TK_CAP / TK1_THREADS; ++i) {
-            const uint32_t idx = (uint32_t)(tid + i * TK1_THREADS);
-            mine[i] = i * TK1_THREADS < ucnt && idx < count ? sh.list[idx] : 0ull;
-        }
-        __syncthreads();
-        if (tid == 0) sh.count = 0;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < TK_CAP / TK1_THREADS; ++i)
-            if (i * TK1_THREADS < ucnt && (uint32_t)(mine[i] >> 32) >= kappa)
-                sh.list[atomicAdd(&sh.count, 1u)] = mine[i];
-        n = (int)(above + n_eq);
-    } else {
-        // the sample misled the threshold: cut by a radix select over the whole row
+        __syncthreads();   // (every thread has read the bins: the general path reuses the memory)
+    }
+
+    // ---- the general path (the sample misled the threshold, or more than
+    // 2048 entries tie at the cut): the cut key kappa, the keys above it and
+    // the keys equal to it from a radix select over the whole row, read again
+    uint32_t kappa, above, n_eq;
+    int n;
+    {
         kappa = radix_select<2>(sh.c, [&](auto fn) {
             for (int i = 0; i < nrows; ++i) {
                 const u32x4 kk = load_keys<VEC>(x, i * TK1_THREADS + tid, V, nchunks);
