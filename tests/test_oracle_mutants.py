@@ -40,8 +40,16 @@ MUTANTS = [
     # shared-prefix decode
     ("suffix of beam 0", SUFFIX_SRC, "const int64_t src = (((r * W + 0) * Ls_cap + j) * nkv + g) * d + e;"),
     ("suffix stride Ls", SUFFIX_SRC, "const int64_t src = (((r * W + b) * Ls + j) * nkv + g) * d + e;"),
-    ("decode heads interleaved", "const int64_t row = (r * W + b) * nq + g * group + hg;",
-     "const int64_t row = (r * W + b) * nq + hg * nkv + g;"),
+    ("decode heads interleaved",
+     "vc[(Lp + j) * d + e] = widen(sv[src]);\n            }\n        for (int32_t hg = 0; hg < group; ++hg) {\n"
+     "            const int64_t row = (r * W + b) * nq + g * group + hg;",
+     "vc[(Lp + j) * d + e] = widen(sv[src]);\n            }\n        for (int32_t hg = 0; hg < group; ++hg) {\n"
+     "            const int64_t row = (r * W + b) * nq + hg * nkv + g;"),
+    ("packed decode heads interleaved",
+     "vc[(lp + j) * d + e] = widen(sv[at]);\n            }\n        for (int32_t hg = 0; hg < group; ++hg) {\n"
+     "            const int64_t row = (r * W + b) * nq + g * group + hg;",
+     "vc[(lp + j) * d + e] = widen(sv[at]);\n            }\n        for (int32_t hg = 0; hg < group; ++hg) {\n"
+     "            const int64_t row = (r * W + b) * nq + hg * nkv + g;"),
     ("prompt of request 0", "kc[u * d + e] = widen(pk[((r * Lp + u) * nkv + g) * d + e]);",
      "kc[u * d + e] = widen(pk[((0 * Lp + u) * nkv + g) * d + e]);"),
     # shared-prefix decode over packed prompts of their own lengths
