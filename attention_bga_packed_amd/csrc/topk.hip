@@ -34,13 +34,16 @@
 // Stage 2 (one workgroup per request): each beam's list is sorted, so only its
 // first min(k_local, k_global) entries can matter and the entries above any
 // threshold form a prefix. A lower bound L on the cut comes from the first 8
-// entries of every beam (two radix digits of their k-th largest); every entry
-// >= L goes into an LDS list (a beam whose 8th entry is >= L continues from
-// memory, 64 entries per wave read); a listed entry's place in the output is
-// the number of larger entries (score desc, flat index asc), counted over runs
-// of 64 sorted in registers by binary searches. When too many
-// entries are >= L (many equal scores), the exact cut comes from radix selects
-// over the beams' prefixes instead, ties by lower flat index.
+// entries of every beam (two radix digits of their k-th largest, or all four
+// when two let more entries in than the list holds); every entry >= L goes
+// into an LDS list of up to 8192 (a beam whose 8th entry is >= L continues
+// from memory, 256 entries per wave read); a radix select over the listed
+// keys gives the exact cut and keeps the k chosen entries (ties by lower flat
+// index); a kept entry's place in the output is the number of larger entries
+// (score desc, flat index asc), counted over runs of 64 sorted in registers by
+// binary searches. When even the exact bound lets more than 8192 entries in
+// (many equal scores), the cut comes from radix selects over the beams'
+// prefixes in memory instead.
 #include <mutex>
 
 #include "bga.h"
@@ -898,30 +901,38 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 
 // ---- stage 2 ----------------------------------------------------------------
 
-constexpr int TK2_LIST = 2048;     // stage 2: candidates sorted in LDS
+constexpr int TK2_LIST = 8192;     // stage 2: candidates listed in LDS (one workgroup per request)
+constexpr int TK2_PER = TK2_LIST / TK2_THREADS;
 
 struct Tk2Shared {
     TkCommon c;
     unsigned long long list[TK2_LIST];             // candidates: key << 32 | ~flat index
+    uint32_t tie[TK2_LIST];                        // ~flat index of the entries whose key is the cut's
     uint32_t whist[TK2_THREADS / 64][256];         // per-wave digit histograms
     uint16_t inc[TK2_THREADS];                     // beams whose list continues above the bound
-    uint32_t count, n_inc;
+    uint32_t count, n_inc, n_tie;
 };
 
 // A lower bound on the k-th largest of the keys kv[0, C) of every thread
-// (each thread's keys descending, 0 = no key; at least k keys in all): that
-// key with its low 16 bits cleared. Two 8-bit digit passes of a radix select,
-// one histogram per wave; a thread counts each run of equal digits with one
-// atomic (its keys are sorted, so the keys that match the prefix and share a
-// digit are adjacent). Keys >= the bound number at least k.
+// (each thread's keys descending, 0 = no key; at least k keys in all): 8-bit
+// digit passes [p0, p1) of a radix select of that key, one histogram per wave;
+// a thread counts each run of equal digits with one atomic (its keys are
+// sorted, so the keys that match the prefix and share a digit are adjacent).
+// After passes [0, p) the bound is the k-th largest key with its low 32 - 8p
+// bits cleared (keys >= it number at least k); the digits found so far stay in
+// `st`, so later passes refine it.
+struct DigitState {
+    uint32_t prefix, mask, krem;
+};
 template <int C>
-__device__ __forceinline__ uint32_t lower_bound16(Tk2Shared &sh, const uint32_t (&kv)[C], uint32_t k)
+__device__ __forceinline__ uint32_t lower_bound_digits(Tk2Shared &sh, const uint32_t (&kv)[C], DigitState &st,
+                                                       int p0, int p1)
 {
     const int tid = threadIdx.x, w = tid >> 6;
     constexpr int NW = TK2_THREADS / 64;
-    uint32_t prefix = 0, mask = 0, krem = k;
+    uint32_t prefix = st.prefix, mask = st.mask, krem = st.krem;
 #pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = p0; pass < p1; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int i = tid; i < NW * 256; i += TK2_THREADS) (&sh.whist[0][0])[i] = 0;
         __syncthreads();
@@ -954,6 +965,7 @@ __device__ __forceinline__ uint32_t lower_bound16(Tk2Shared &sh, const uint32_t 
         mask |= 255u << shift;
         __syncthreads();
     }
+    st = DigitState{prefix, mask, krem};
     return prefix;
 }
 
@@ -978,61 +990,80 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
     };
 
     // -- a lower bound L on the cut: the k-th largest of the first C entries of
-    // every beam, its low 16 bits cleared (a subset of the candidates holds k
-    // keys >= L, so the k-th largest of all of them is >= L)
+    // every beam, or that key with its low 16 bits cleared (a subset of the
+    // candidates holds k keys >= L, so the k-th largest of all of them is >= L)
     constexpr int C = 8;
     const int cb = min(kk, C);
     uint32_t kv[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) kv[j] = (has_beam && j < cb) ? key32(brow[j]) : 0u;   // 0: nothing (finite keys > 0)
-    uint32_t L = 1u;   // every entry
-    if ((long long)W_in * cb >= (long long)k) L = max(lower_bound16(sh, kv, k), 1u);
-
     // -- every entry >= L goes into the list: the first C from registers; a
     // beam whose C-th entry is still >= L continues in memory (its list is
     // sorted, so its entries >= L form a prefix), read 64 at a time by a wave
-    if (tid == 0) {
-        sh.count = 0;
-        sh.n_inc = 0;
-    }
-    __syncthreads();
-    uint32_t nreg = 0;
-#pragma unroll
-    for (int j = 0; j < C; ++j) nreg += kv[j] >= L ? 1u : 0u;
-    if (nreg) {
-        uint32_t at = atomicAdd(&sh.count, nreg);
-#pragma unroll
-        for (int j = 0; j < C; ++j)
-            if (kv[j] >= L) {
-                if (at < (uint32_t)TK2_LIST) sh.list[at] = entry(kv[j], b, j);
-                ++at;
-            }
-    }
-    if (has_beam && cb < kk && kv[cb - 1] >= L) sh.inc[atomicAdd(&sh.n_inc, 1u)] = (uint16_t)b;
-    __syncthreads();
-    const int n_inc = (int)sh.n_inc;
-    for (int t = w; t < n_inc; t += TK2_THREADS / 64) {
-        const int bb = sh.inc[t];
-        const float *row = sc + (size_t)bb * k_local;
-        for (int j0 = C; j0 < kk; j0 += 64) {
-            const int j = j0 + lane;
-            const uint32_t key = j < kk ? key32(row[j]) : 0u;
-            const bool take = key >= L;
-            const unsigned long long mask = __ballot(take);
-            const uint32_t cnt = (uint32_t)__popcll(mask);
-            uint32_t base = 0;
-            if (lane == 0 && cnt) base = atomicAdd(&sh.count, cnt);
-            base = (uint32_t)__shfl((int)base, 0);
-            if (take) {
-                const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                if (pos < (uint32_t)TK2_LIST) sh.list[pos] = entry(key, bb, j);
-            }
-            if (cnt < 64u) break;   // the rest of this beam is below L
+    auto build_list = [&](uint32_t L) {
+        if (tid == 0) {
+            sh.count = 0;
+            sh.n_inc = 0;
         }
-    }
-    __syncthreads();
-    const uint32_t n = sh.count;   // >= k
+        __syncthreads();
+        uint32_t nreg = 0;
+#pragma unroll
+        for (int j = 0; j < C; ++j) nreg += kv[j] >= L ? 1u : 0u;
+        if (nreg) {
+            uint32_t at = atomicAdd(&sh.count, nreg);
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                if (kv[j] >= L) {
+                    if (at < (uint32_t)TK2_LIST) sh.list[at] = entry(kv[j], b, j);
+                    ++at;
+                }
+        }
+        if (has_beam && cb < kk && kv[cb - 1] >= L) sh.inc[atomicAdd(&sh.n_inc, 1u)] = (uint16_t)b;
+        __syncthreads();
+        const int n_inc = (int)sh.n_inc;
+        for (int t = w; t < n_inc; t += TK2_THREADS / 64) {
+            const int bb = sh.inc[t];
+            const float *row = sc + (size_t)bb * k_local;
+            // four runs of 64 per round trip (the loads of a round go out together)
+            for (int j0 = C; j0 < kk; j0 += 256) {
+                uint32_t key[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = j0 + 64 * u + lane;
+                    key[u] = j < kk ? key32(row[j]) : 0u;
+                }
+                bool more = true;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = j0 + 64 * u + lane;
+                    const bool take = more && key[u] >= L;
+                    const unsigned long long mask = __ballot(take);
+                    const uint32_t cnt = (uint32_t)__popcll(mask);
+                    uint32_t base = 0;
+                    if (lane == 0 && cnt) base = atomicAdd(&sh.count, cnt);
+                    base = (uint32_t)__shfl((int)base, 0);
+                    if (take) {
+                        const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(
+                                                        (uint32_t)(mask >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                        if (pos < (uint32_t)TK2_LIST) sh.list[pos] = entry(key[u], bb, j);
+                    }
+                    more = more && cnt == 64u;   // a run not wholly >= L ends the beam's prefix
+                }
+                if (!more) break;
+            }
+        }
+        __syncthreads();
+        return sh.count;
+    };
+    // The bound first keeps the key's top 16 bits; if that lets more entries in
+    // than the list holds (scores crowded near the cut, as after the first
+    // step, when every beam descends from one), two more digits make it the
+    // exact k-th largest of the first C entries and the list is built again.
+    DigitState st{0u, 0u, k};
+    const bool bounded = (long long)W_in * cb >= (long long)k;
+    uint32_t n = build_list(bounded ? max(lower_bound_digits(sh, kv, st, 0, 2), 1u) : 1u);
+    if (bounded && n > (uint32_t)TK2_LIST) n = build_list(max(lower_bound_digits(sh, kv, st, 2, 4), 1u));
 
     if (n > (uint32_t)TK2_LIST) {
         // Many entries at or above L (for example, many equal scores): the
@@ -1079,6 +1110,76 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
         if (take > 0) {
             const uint32_t slot0 = atomicAdd(&sh.count, (uint32_t)take);
             for (int j = 0; j < take; ++j) sh.list[slot0 + j] = entry(key32(brow[j]), b, j);
+        }
+        __syncthreads();
+    } else if (n > k) {
+        // More entries listed than chosen: the exact cut kappa among them (a
+        // radix select over the listed keys, per-wave histograms), then only
+        // the k chosen stay listed (keys above kappa, and of the keys equal to
+        // it those with the lowest flat indices), so that the ordering below
+        // ranks k entries, not n.
+        unsigned long long e[TK2_PER];
+#pragma unroll
+        for (int q = 0; q < TK2_PER; ++q) {
+            const uint32_t i = (uint32_t)(tid + q * TK2_THREADS);
+            e[q] = i < n ? sh.list[i] : 0ull;   // 0: no entry (finite keys > 0)
+        }
+        uint32_t prefix = 0, mask = 0, krem = k, above = 0, n_eq = 0;
+#pragma unroll 1
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int i = tid; i < (TK2_THREADS / 64) * 256; i += TK2_THREADS) (&sh.whist[0][0])[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < TK2_PER; ++q) {
+                const uint32_t key = (uint32_t)(e[q] >> 32);
+                if (key && (key & mask) == prefix) atomicAdd(&sh.whist[w][(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int i = 0; i < TK2_THREADS / 64; ++i) c += sh.whist[i][tid];
+                sh.c.hist[tid] = c;
+            }
+            __syncthreads();
+            select_bin(sh.c, sh.c.hist, krem);
+            above += sh.c.bcast[1];
+            krem -= sh.c.bcast[1];
+            n_eq = sh.c.bcast[2];
+            prefix |= sh.c.bcast[0] << shift;
+            mask |= 255u << shift;
+            __syncthreads();
+        }
+        const uint32_t kappa = prefix, need = k - above;   // 1 <= need <= n_eq
+        // ties: when only some of the entries equal to kappa are chosen, an
+        // entry's rank among them is the number with a lower flat index
+        if (tid == 0) {
+            sh.count = 0;
+            sh.n_tie = 0;
+        }
+        __syncthreads();
+        if (need < n_eq) {
+#pragma unroll
+            for (int q = 0; q < TK2_PER; ++q)
+                if ((uint32_t)(e[q] >> 32) == kappa) sh.tie[atomicAdd(&sh.n_tie, 1u)] = (uint32_t)e[q];
+            __syncthreads();
+        }
+        const uint32_t nt = sh.n_tie;
+#pragma unroll
+        for (int q = 0; q < TK2_PER; ++q) {
+            const uint32_t key = (uint32_t)(e[q] >> 32);
+            bool keep = key > kappa;
+            if (key == kappa) {
+                if (need >= n_eq) {
+                    keep = true;
+                } else {
+                    uint32_t rank = 0;   // lower flat index <=> larger complemented index
+                    for (uint32_t i = 0; i < nt; ++i) rank += sh.tie[i] > (uint32_t)e[q] ? 1u : 0u;
+                    keep = rank < need;
+                }
+            }
+            if (keep) sh.list[atomicAdd(&sh.count, 1u)] = e[q];
         }
         __syncthreads();
     }
