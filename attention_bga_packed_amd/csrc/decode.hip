@@ -202,8 +202,8 @@ static hipError_t launch_decode_d(const uint16_t *q, const uint16_t *pk, const u
     const int group = nq / nkv;
     const int rows = W * group;
     const size_t smem = Geo<D>::SMEM;
-    hipError_t e = hipFuncSetAttribute((const void *)shared_prefix_decode_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = dynamic_lds_once((const void *)shared_prefix_decode_kernel<D>, (int)smem, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid(R * nkv, (rows + 127) / 128), block(256);
     hipLaunchKernelGGL(shared_prefix_decode_kernel<D>, grid, block, smem, stream, q, pk, pv, pcu, sk, sv, W, Lp,

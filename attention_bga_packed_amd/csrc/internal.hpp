@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bga {
 
 // Every launcher returns hipSuccess or the launch error.
@@ -77,5 +79,19 @@ hipError_t debug_check_prompts(const int32_t *cu, int R, int T, int max_len, boo
 hipError_t debug_check_parents(const int32_t *parent, int n, int W, hipStream_t stream, uint32_t *violations);
 hipError_t debug_check_logits(const uint16_t *x, size_t n, hipStream_t stream, uint32_t *violations);
 #endif
+
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per device: `done`
+// (one per kernel) keeps a bit per device that has been set up.
+inline hipError_t dynamic_lds_once(const void *kern, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 }  // namespace bga

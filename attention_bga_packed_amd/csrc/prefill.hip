@@ -124,7 +124,8 @@ static hipError_t launch_prefill_d(const uint16_t *q, const uint16_t *k, const u
     const int blocks_y = (int)(((int64_t)max_seqlen * group + 32 * NW - 1) / (32 * NW));
     const size_t smem = Geo<D>::SMEM;
     const void *kern = (const void *)packed_prefill_kernel<D, NW>;
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = dynamic_lds_once(kern, (int)smem, lds_set);
     if (e != hipSuccess) return e;
     // Pair-major order for grids several times what the GPU holds at once whose sequences are (nearly) all
     // of the longest length: every pair's blocks are then alike and each XCD's L2 keeps its current pairs'

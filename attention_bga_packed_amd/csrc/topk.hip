@@ -1112,12 +1112,13 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
             for (int j = 0; j < take; ++j) sh.list[slot0 + j] = entry(key32(brow[j]), b, j);
         }
         __syncthreads();
-    } else if (n > k) {
-        // More entries listed than chosen: the exact cut kappa among them (a
-        // radix select over the listed keys, per-wave histograms), then only
+    } else if (n > k + 512u) {
+        // Many more entries listed than chosen: the exact cut kappa among them
+        // (a radix select over the listed keys, per-wave histograms), then only
         // the k chosen stay listed (keys above kappa, and of the keys equal to
         // it those with the lowest flat indices), so that the ordering below
-        // ranks k entries, not n.
+        // ranks k entries, not n. (A few more than k are cheaper to order
+        // than to cut.)
         unsigned long long e[TK2_PER];
 #pragma unroll
         for (int q = 0; q < TK2_PER; ++q) {
