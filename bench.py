@@ -58,9 +58,21 @@ KERNEL_SOURCES = {
     "shared_prefix_decode": ["decode.hip", "attn_core.hpp", "device_common.hpp", "internal.hpp"],
     "beam_topk": ["topk.hip", "device_common.hpp", "internal.hpp"],
     "suffix_reorder": ["reorder.hip", "internal.hpp"],
+    "swiglu_quant": ["swiglu_fp8.hip", "device_common.hpp", "internal.hpp"],
 }
 # workload -> {"kernel", "fetch_kib", "write_kib", "sources_sha256"}
-MEASURED_TRAFFIC: dict = {}
+# (measured with the command lines in profiles/hbm_counters_by_workload.md)
+MEASURED_TRAFFIC: dict = {
+    "prefill_only": {"kernel": "packed_gqa_prefill", "fetch_kib": 17135.2, "write_kib": 17972.3, "sources_sha256": "e9abfae5b6580973"},
+    "long_prefill": {"kernel": "packed_gqa_prefill", "fetch_kib": 62363.0, "write_kib": 112737.9, "sources_sha256": "e9abfae5b6580973"},
+    "long_prefill_1024": {"kernel": "packed_gqa_prefill", "fetch_kib": 139672.7, "write_kib": 252321.0, "sources_sha256": "e9abfae5b6580973"},
+    "short_decode/decode": {"kernel": "shared_prefix_decode", "fetch_kib": 15425.6, "write_kib": 7200.0, "sources_sha256": "6f5b3400c5b60814"},
+    "short_decode/reorder": {"kernel": "suffix_reorder", "fetch_kib": 7693.0, "write_kib": 16000.0, "sources_sha256": "cebdd1b87cc1b27b"},
+    "long_beam/decode": {"kernel": "shared_prefix_decode", "fetch_kib": 34381.4, "write_kib": 15392.0, "sources_sha256": "6f5b3400c5b60814"},
+    "long_beam/reorder": {"kernel": "suffix_reorder", "fetch_kib": 14415.2, "write_kib": 38400.0, "sources_sha256": "cebdd1b87cc1b27b"},
+    "long_beam/topk": {"kernel": "beam_topk", "fetch_kib": 487182.2, "write_kib": 20037.5, "sources_sha256": "8d899b4953f02147"},
+    "swiglu_fp8": {"kernel": "swiglu_quant", "fetch_kib": 33840.6, "write_kib": 17044.2, "sources_sha256": "2156f9de1d0a04e0"},
+}
 
 
 def sources_sha(kernel):
