@@ -144,6 +144,28 @@ class Timer:
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
+    def per_launch_us(self, fns, n):
+        """p10 / p50 / p90 of single launches (µs): n back-to-back calls cycling over fns behind the
+        same gate, an event recorded between consecutive calls."""
+        torch = self.torch
+        fns[0]()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        t0 = time.perf_counter()
+        for i in range(n):
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda._sleep(int(self.cycles_per_ms * max(3.0 * host_ms, 2.0)))
+        evs[0].record(self.stream)
+        for i in range(n):
+            fns[i % len(fns)]()
+            evs[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        d = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n))
+        pick = lambda q: round(d[min(n - 1, int(q * (n - 1) + 0.5))], 2)
+        return {"launch_us_p10": pick(0.1), "launch_us_p50": pick(0.5), "launch_us_p90": pick(0.9), "launches": n}
+
 
 def build_inputs(dev, only=None):
     """Every workload's inputs and launch closures, resident in HBM. Returns {workload: dict}."""
@@ -409,6 +431,7 @@ def main():
         n = len(w["fns"]) * max(1, K // len(w["fns"])) if name == "prefill_only" else max(K, 2 * len(w["fns"]))
         ms = timer.span_ms(w["fns"], n) / n
         rooflines[name] = prefill_roofline(name, w, ms)
+        rooflines[name].update(timer.per_launch_us(w["fns"], max(n, 20)))
     if "prefill_only" in W:
         w, cfg = W["prefill_only"], W["prefill_only"]["cfg"]
         n = max(K, 8)
@@ -424,6 +447,7 @@ def main():
         b = wl.swiglu_quant_bytes(cfg["tokens"], cfg["inter"])
         r = roof("hbm", b / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", b, ms, measured_traffic("swiglu_fp8"))
         r.update({"kernel": "swiglu_quant_kernel"})
+        r.update(timer.per_launch_us(w["fns"], max(n, 20)))
         rooflines["swiglu_fp8"] = r
     if "long_beam_loop" in W:
         w = W["long_beam_loop"]
@@ -448,6 +472,8 @@ def main():
         gbs = sum(dec_b) / (sum(dec_ms) * 1e-3) / 1e9
         r = roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(dec_b)), float(np.mean(dec_ms)),
                  measured_traffic(f"{name}/decode"))
+        pl = [timer.per_launch_us(w["decode"][s], max(n, 10)) for s in range(NS)]
+        r.update({k: [x[k] for x in pl] for k in ("launch_us_p10", "launch_us_p50", "launch_us_p90")})
         r.update({"kernel": "shared_prefix_decode_kernel", "us_per_step": [round(t * 1e3, 2) for t in dec_ms],
                   "mfma_tflops": round(sum(dec_f) / (sum(dec_ms) * 1e-3) / 1e12, 2),
                   "mfma_frac": round(sum(dec_f) / (sum(dec_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
@@ -455,6 +481,8 @@ def main():
         gbs = sum(reo_b) / (sum(reo_ms) * 1e-3) / 1e9
         r = roof("hbm", gbs, PEAK_HBM_GBS, "GB/s", int(np.mean(reo_b)), float(np.mean(reo_ms)),
                  measured_traffic(f"{name}/reorder"))
+        pl = [timer.per_launch_us(w["reorder"][s], max(n, 10)) for s in range(NS)]
+        r.update({k: [x[k] for x in pl] for k in ("launch_us_p10", "launch_us_p50", "launch_us_p90")})
         r.update({"kernel": "suffix_reorder_kernel", "us_per_step": [round(t * 1e3, 2) for t in reo_ms]})
         rooflines[f"{name}/reorder"] = r
         if "topk" in w:
@@ -463,6 +491,7 @@ def main():
             b = wl.topk_bytes(R, Wb, cfg["vocab"], Wb)
             r = roof("hbm", b / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", b, ms, measured_traffic(f"{name}/topk"))
             r.update({"kernel": "topk_stage1_kernel + topk_stage2_kernel"})
+            r.update(timer.per_launch_us(w["topk"], max(n, 10)))
             rooflines[f"{name}/topk"] = r
 
     headline = "long_prefill_1024" if "long_prefill_1024" in rooflines else next(iter(rooflines))
