@@ -80,11 +80,21 @@ __device__ __forceinline__ float key16_value(uint32_t key)
     return __uint_as_float(b << 16);
 }
 
+__device__ __forceinline__ float key32_value(uint64_t key64);
+
 __device__ __forceinline__ uint32_t key32(float f)
 {
     uint32_t b = __float_as_uint(f);
     b = (b == 0x80000000u) ? 0u : b;
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// The score of a 32-bit key (every finite score but -0 maps back to itself;
+// -0 was keyed as +0).
+__device__ __forceinline__ float key32_value(uint64_t key64)
+{
+    const uint32_t key = (uint32_t)key64;
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 // ---- block-wide helpers ------------------------------------------------------
@@ -904,9 +914,16 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 constexpr int TK2_LIST = 8192;     // stage 2: candidates listed in LDS (one workgroup per request)
 constexpr int TK2_PER = TK2_LIST / TK2_THREADS;
 
+// A listed stage-2 entry: key << 32 | (2^19 - 1 - flat index) << 13 | list slot
+// (flat index = beam * k_local + slot < 2^19; list slot < 8192). Entries order
+// by (score desc, flat index asc); the list slot names the entry's token,
+// loaded when it is listed, so the output needs no second read of memory.
+static_assert(BGA_MAX_BEAMS * BGA_MAX_K <= (1 << 19) && TK2_LIST <= (1 << 13), "stage-2 entry fields");
+
 struct Tk2Shared {
     TkCommon c;
-    unsigned long long list[TK2_LIST];             // candidates: key << 32 | ~flat index
+    unsigned long long list[TK2_LIST];             // candidates (entries as above)
+    int32_t tok[TK2_LIST];                         // token of the entry listed at each slot
     uint32_t tie[TK2_LIST];                        // ~flat index of the entries whose key is the cut's
     uint32_t whist[TK2_THREADS / 64][256];         // per-wave digit histograms
     uint16_t inc[TK2_THREADS];                     // beams whose list continues above the bound
@@ -985,8 +1002,9 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
     const int b = tid;                       // one beam per thread (W_in <= 1024)
     const bool has_beam = b < W_in;
     const float *brow = sc + (size_t)(has_beam ? b : 0) * k_local;
-    auto entry = [&](uint32_t key, int beam, int j) {
-        return ((unsigned long long)key << 32) | (0xffffffffu - (uint32_t)(beam * k_local + j));
+    const int32_t *tk = ws_tok + (size_t)r * W_in * k_local;
+    auto entry = [&](uint32_t key, int beam, int j, uint32_t slot) {
+        return ((unsigned long long)key << 32) | ((0x7ffffu - (uint32_t)(beam * k_local + j)) << 13) | slot;
     };
 
     // -- a lower bound L on the cut: the k-th largest of the first C entries of
@@ -1014,7 +1032,10 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
 #pragma unroll
             for (int j = 0; j < C; ++j)
                 if (kv[j] >= L) {
-                    if (at < (uint32_t)TK2_LIST) sh.list[at] = entry(kv[j], b, j);
+                    if (at < (uint32_t)TK2_LIST) {
+                        sh.list[at] = entry(kv[j], b, j, at);
+                        sh.tok[at] = tk[(size_t)b * k_local + j];
+                    }
                     ++at;
                 }
         }
@@ -1046,7 +1067,10 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
                         const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(
                                                         (uint32_t)(mask >> 32),
                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                        if (pos < (uint32_t)TK2_LIST) sh.list[pos] = entry(key[u], bb, j);
+                        if (pos < (uint32_t)TK2_LIST) {
+                            sh.list[pos] = entry(key[u], bb, j, pos);
+                            sh.tok[pos] = tk[(size_t)bb * k_local + j];
+                        }
                     }
                     more = more && cnt == 64u;   // a run not wholly >= L ends the beam's prefix
                 }
@@ -1109,7 +1133,10 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
         const int take = gt_end + take_ties;
         if (take > 0) {
             const uint32_t slot0 = atomicAdd(&sh.count, (uint32_t)take);
-            for (int j = 0; j < take; ++j) sh.list[slot0 + j] = entry(key32(brow[j]), b, j);
+            for (int j = 0; j < take; ++j) {
+                sh.list[slot0 + j] = entry(key32(brow[j]), b, j, slot0 + (uint32_t)j);
+                sh.tok[slot0 + j] = tk[(size_t)b * k_local + j];
+            }
         }
         __syncthreads();
     } else if (n > k + 512u) {
@@ -1229,12 +1256,11 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
             }
         }
         if (place < k) {
-            const uint32_t f = 0xffffffffu - (uint32_t)(e & 0xffffffffu);
-            const int parent = (int)(f / (uint32_t)k_local), j = (int)(f % (uint32_t)k_local);
-            const size_t src = ((size_t)r * W_in + parent) * k_local + j;
-            out_tok[(size_t)r * k_global + place] = ws_tok[src];
-            out_par[(size_t)r * k_global + place] = parent;
-            out_score[(size_t)r * k_global + place] = ws_score[src];
+            const uint32_t low = (uint32_t)e;
+            const uint32_t f = 0x7ffffu - (low >> 13);
+            out_tok[(size_t)r * k_global + place] = sh.tok[low & 0x1fffu];
+            out_par[(size_t)r * k_global + place] = (int)(f / (uint32_t)k_local);
+            out_score[(size_t)r * k_global + place] = key32_value(e >> 32);
         }
     }
 }
