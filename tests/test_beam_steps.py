@@ -54,6 +54,9 @@ def host(t):
     ((5, 40, 130), 8, 5, 1000, 4, 2, 64, 3, 0.3, 2.0),
     ((180, 240, 97, 256), 64, 6, 32000, 16, 8, 128, 151, 0.1, 3.0),
     ((33, 70), 200, 4, 5000, 14, 2, 64, 0, 0.2, 3.0),
+    # the long-prompt configuration's beam width and vocabulary: 400 beams of one parent after the first step,
+    # scores crowded near the cut (the 8192-entry list and exact cut of the global selection)
+    ((64, 200), 400, 4, 151936, 16, 8, 128, 2, 0.05, 3.0),
 ])
 def test_beam_search_steps_against_the_oracle(lengths, W, n_gen, V, nq, nkv, d, eos, boost, std):
     import attention_bga_packed_amd as bga
