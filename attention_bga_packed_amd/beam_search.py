@@ -18,6 +18,12 @@ The model between decode and select (its outputs are the query, the new
 token's K/V and the logits) is not part of this path; callers pass its outputs.
 The prompts' K/V are the packed prefill's K/V, used as the shared prefix as they
 are (prompt_cu gives each request's rows).
+
+Every call works in the state allocated here (the final ranking's buffers
+after the first finish()), clears nothing and never waits on the host, so once
+a loop has run, a whole loop can be captured into a HIP graph
+(torch.cuda.graph) and replayed; a replay reads the model outputs from the
+tensors the capture saw.
 """
 from __future__ import annotations
 

@@ -150,3 +150,59 @@ def test_beam_search_steps_against_the_oracle(lengths, W, n_gen, V, nq, nkv, d, 
     say(f"    {n_gen} steps identical; finished hypotheses {n_fin}; requests whose own-lse selection differs at "
         f"the cut: {n_cut} (largest gap {worst_gap:.2f} ulp)")
     assert boost == 0 or n_fin > 0
+
+
+def test_beam_search_replays_as_a_graph():
+    """The whole loop allocates nothing, clears nothing and never waits on the host once its state exists, so it
+    can be captured once (HIP stream capture through torch.cuda.graph) and replayed: every replay, with eager work
+    and synchronisations between them, gives the final ranking of the eager loop bit for bit."""
+    from attention_bga_packed_amd.beam_search import BeamSearch
+
+    lengths, W, n_gen, V, nq, nkv, d, eos = (40, 130), 16, 5, 3000, 8, 4, 64, 3
+    R = len(lengths)
+    cu = torch.from_numpy(wl.cu_seqlens_from_lengths(lengths)).to(DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    tp = sum(lengths)
+    pk = wl.bf16_normal((tp, nkv, d), g, DEV)
+    pv = wl.bf16_normal((tp, nkv, d), g, DEV)
+    model = synthetic_model(R, W, V, nq, nkv, d, eos, n_gen, seed=17, boost=0.2, std=3.0)
+    bs = BeamSearch(R, W, n_gen, V, nq, nkv, d, eos, DEV)
+
+    def loop():
+        bs.start(pk, pv, cu, model[0]["logits"])
+        for s in range(1, n_gen):
+            m = model[s]
+            bs.decode(m["q"], m["k"], m["v"])
+            bs.select(m["logits"])
+        return bs.finish()
+
+    say(f"[beam loop graph] R={R} W={W} N_gen={n_gen} V={V}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # eager runs (the first one sizes the final ranking's buffers)
+        loop()
+        ref = {k: v.clone() for k, v in loop().items()}
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in bs.final.values():
+            t.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in bs.final.items()}
+        want = {k: host(v) for k, v in ref.items()}
+        assert torch.equal(got["count"], want["count"]), rep
+        for r in range(R):   # the ranking fills the first count entries of each request
+            n = int(want["count"][r])
+            assert torch.equal(got["scores"][r, :n], want["scores"][r, :n]), (rep, r)
+            assert torch.equal(got["lengths"][r, :n], want["lengths"][r, :n]), (rep, r)
+            for i in range(n):
+                ln = int(want["lengths"][r, i])
+                assert torch.equal(got["tokens"][r, i, :ln], want["tokens"][r, i, :ln]), (rep, r, i)
+        assert torch.randn(256, device=DEV).abs().sum().item() > 0   # eager work between replays
