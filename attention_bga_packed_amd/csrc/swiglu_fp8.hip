@@ -38,8 +38,9 @@ __global__ __launch_bounds__(SQ_THREADS) void swiglu_quant_kernel(const u32x4 *_
     for (int k = 0; k < NCH; ++k) {
         const int c = k * SQ_THREADS + tid;
         const bool ok = c < nch;
-        g[k] = ok ? gate[c] : u32x4{0u, 0u, 0u, 0u};
-        u[k] = ok ? up[c] : u32x4{0u, 0u, 0u, 0u};
+        // read once: non-temporal
+        g[k] = ok ? __builtin_nontemporal_load(gate + c) : u32x4{0u, 0u, 0u, 0u};
+        u[k] = ok ? __builtin_nontemporal_load(up + c) : u32x4{0u, 0u, 0u, 0u};
     }
     float h[NCH][8];
     float amax = 0.f;

@@ -413,7 +413,9 @@ __device__ __forceinline__ u32x4 load_raw(const uint16_t *__restrict__ x, int c,
 {
     u32x4 raw;
     if (VEC) {
-        raw = *(const u32x4 *)(x + (size_t)min(c, nchunks - 1) * 8);
+        // every logit is read once: the non-temporal hint keeps the stream
+        // from displacing what other workgroups still use in the caches
+        raw = __builtin_nontemporal_load((const u32x4 *)(x + (size_t)min(c, nchunks - 1) * 8));
         if (c >= nchunks) raw = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
     } else {
 #pragma unroll

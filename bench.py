@@ -70,8 +70,8 @@ MEASURED_TRAFFIC: dict = {
     "short_decode/reorder": {"kernel": "suffix_reorder", "fetch_kib": 7693.0, "write_kib": 16000.0, "sources_sha256": "cebdd1b87cc1b27b"},
     "long_beam/decode": {"kernel": "shared_prefix_decode", "fetch_kib": 34381.4, "write_kib": 15392.0, "sources_sha256": "6f5b3400c5b60814"},
     "long_beam/reorder": {"kernel": "suffix_reorder", "fetch_kib": 14415.2, "write_kib": 38400.0, "sources_sha256": "cebdd1b87cc1b27b"},
-    "long_beam/topk": {"kernel": "beam_topk", "fetch_kib": 487171.0, "write_kib": 20037.5, "sources_sha256": "248bd772471b7583"},
-    "swiglu_fp8": {"kernel": "swiglu_quant", "fetch_kib": 33840.6, "write_kib": 17044.2, "sources_sha256": "2156f9de1d0a04e0"},
+    "long_beam/topk": {"kernel": "beam_topk", "fetch_kib": 475898.1, "write_kib": 20037.5, "sources_sha256": "786fecead2b265f9"},
+    "swiglu_fp8": {"kernel": "swiglu_quant", "fetch_kib": 33840.5, "write_kib": 17044.1, "sources_sha256": "58bd510a4b1ecb4f"},
 }
 
 
