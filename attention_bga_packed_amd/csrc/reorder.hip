@@ -46,9 +46,9 @@ __global__ __launch_bounds__(256) void suffix_reorder_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = i0 + u * 256 + (int)threadIdx.x;
-            if (i < run16) {
-                dk[i] = a[u];
-                dv[i] = b[u];
+            if (i < run16) {   // non-temporal: the next step reads them once, in another kernel
+                __builtin_nontemporal_store(a[u], dk + i);
+                __builtin_nontemporal_store(b[u], dv + i);
             }
         }
     }

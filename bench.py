@@ -67,9 +67,9 @@ MEASURED_TRAFFIC: dict = {
     "long_prefill": {"kernel": "packed_gqa_prefill", "fetch_kib": 62363.0, "write_kib": 112737.9, "sources_sha256": "e9abfae5b6580973"},
     "long_prefill_1024": {"kernel": "packed_gqa_prefill", "fetch_kib": 139672.7, "write_kib": 252321.0, "sources_sha256": "e9abfae5b6580973"},
     "short_decode/decode": {"kernel": "shared_prefix_decode", "fetch_kib": 15425.6, "write_kib": 7200.0, "sources_sha256": "6f5b3400c5b60814"},
-    "short_decode/reorder": {"kernel": "suffix_reorder", "fetch_kib": 7693.0, "write_kib": 16000.0, "sources_sha256": "cebdd1b87cc1b27b"},
+    "short_decode/reorder": {"kernel": "suffix_reorder", "fetch_kib": 7693.0, "write_kib": 16024.9, "sources_sha256": "e0ef6d4301e3490d"},
     "long_beam/decode": {"kernel": "shared_prefix_decode", "fetch_kib": 34381.4, "write_kib": 15392.0, "sources_sha256": "6f5b3400c5b60814"},
-    "long_beam/reorder": {"kernel": "suffix_reorder", "fetch_kib": 14415.2, "write_kib": 38400.0, "sources_sha256": "cebdd1b87cc1b27b"},
+    "long_beam/reorder": {"kernel": "suffix_reorder", "fetch_kib": 14329.8, "write_kib": 38460.5, "sources_sha256": "e0ef6d4301e3490d"},
     "long_beam/topk": {"kernel": "beam_topk", "fetch_kib": 475898.1, "write_kib": 20037.5, "sources_sha256": "786fecead2b265f9"},
     "swiglu_fp8": {"kernel": "swiglu_quant", "fetch_kib": 33840.5, "write_kib": 17044.1, "sources_sha256": "58bd510a4b1ecb4f"},
 }
