@@ -37,13 +37,13 @@
 // entries of every beam (two radix digits of their k-th largest, or all four
 // when two let more entries in than the list holds); every entry >= L goes
 // into an LDS list of up to 8192 (a beam whose 8th entry is >= L continues
-// from memory, 256 entries per wave read); a radix select over the listed
-// keys gives the exact cut and keeps the k chosen entries (ties by lower flat
-// index); a kept entry's place in the output is the number of larger entries
-// (score desc, flat index asc), counted over runs of 64 sorted in registers by
-// binary searches. When even the exact bound lets more than 8192 entries in
-// (many equal scores), the cut comes from radix selects over the beams'
-// prefixes in memory instead.
+// from memory, 256 entries per wave read); when more than 2048 are listed, a
+// radix select over the listed keys gives the exact cut and keeps the k
+// chosen entries (ties by lower flat index); the listed entries (at most 2048)
+// are then sorted by (score desc, flat index asc) with one bitonic network and
+// the first k are the output. When even the exact bound lets more than 8192
+// entries in (many equal scores), the cut comes from radix selects over the
+// beams' prefixes in memory instead.
 #include <mutex>
 
 #include "bga.h"
@@ -915,6 +915,8 @@ __global__ __launch_bounds__(TK1_THREADS) void topk_stage1_kernel(const uint16_t
 
 constexpr int TK2_LIST = 8192;     // stage 2: candidates listed in LDS (one workgroup per request)
 constexpr int TK2_PER = TK2_LIST / TK2_THREADS;
+constexpr int TK2_SORT = 2 * TK2_THREADS;   // places of the final bitonic sort
+static_assert(BGA_MAX_K <= TK2_SORT, "the sort holds every chosen entry");
 
 // A listed stage-2 entry: key << 32 | (2^19 - 1 - flat index) << 13 | list slot
 // (flat index = beam * k_local + slot < 2^19; list slot < 8192). Entries order
@@ -1141,13 +1143,13 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
             }
         }
         __syncthreads();
-    } else if (n > k + 512u) {
+    } else if (n > (uint32_t)TK2_SORT) {
         // Many more entries listed than chosen: the exact cut kappa among them
         // (a radix select over the listed keys, per-wave histograms), then only
         // the k chosen stay listed (keys above kappa, and of the keys equal to
         // it those with the lowest flat indices), so that the ordering below
-        // ranks k entries, not n. (A few more than k are cheaper to order
-        // than to cut.)
+        // sorts k entries, not n. (Up to 2048 listed entries are sorted as
+        // they are.)
         unsigned long long e[TK2_PER];
 #pragma unroll
         for (int q = 0; q < TK2_PER; ++q) {
@@ -1214,57 +1216,72 @@ __global__ __launch_bounds__(TK2_THREADS) void topk_stage2_kernel(const int32_t 
         __syncthreads();
     }
 
-    // -- order: the place of a listed entry is the number of larger entries
-    // (entries are distinct, the flat index being part of them; equal scores
-    // order by the complemented index: lower index first). The list is cut into
-    // runs of 64, each sorted by one wave in registers; an entry's place is
-    // the sum over all runs of their entries above it, found by binary search
-    // (in its own run that is its lane).
-    const int m = (int)min(sh.count, (uint32_t)TK2_LIST);   // >= k
-    const int nrun = (m + 63) / 64;
-    for (int i = m + tid; i < nrun * 64; i += TK2_THREADS) sh.list[i] = 0ull;   // 0: below every entry
-    __syncthreads();
-    for (int q = w; q < nrun; q += TK2_THREADS / 64) {
-        unsigned long long v = sh.list[q * 64 + lane];
+    // -- order: the m <= 2048 listed entries (distinct: the flat index is part
+    // of each; equal scores order by the complemented index, lower index first)
+    // are sorted in descending order by a bitonic network over N = 1024 or 2048
+    // places, N / 1024 per thread (places tid and tid + 1024), 0 padding the
+    // list (below every entry). Distances below 64 are lane exchanges, 1024
+    // stays inside the thread, the others go through the list in LDS; place
+    // p < k of the sorted list is place p of the output.
+    const int m = (int)min(sh.count, (uint32_t)TK2_SORT);   // >= k
+    auto sort_and_store = [&](auto places) {
+        constexpr int N = decltype(places)::value;
+        constexpr int NPT = N / TK2_THREADS;
+        unsigned long long v[NPT];
 #pragma unroll
-        for (int size = 2; size <= 64; size <<= 1)
+        for (int h = 0; h < NPT; ++h) {
+            const int p = tid + h * TK2_THREADS;
+            v[h] = p < m ? sh.list[p] : 0ull;
+        }
+        __syncthreads();   // every listed entry is in registers: the list serves the exchanges
 #pragma unroll
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const uint32_t lo = lane_xor((uint32_t)v, stride), hi = lane_xor((uint32_t)(v >> 32), stride);
-                const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-                const bool take_max = ((lane & stride) == 0) == ((lane & size) == 0);
-                v = take_max ? (v > o ? v : o) : (v < o ? v : o);
+        for (int k2 = 2; k2 <= N; k2 <<= 1)
+#pragma unroll
+            for (int j = k2 >> 1; j > 0; j >>= 1) {
+                unsigned long long o[NPT];
+                if (j == TK2_THREADS) {   // places tid and tid + 1024: the same thread
+                    o[0] = v[NPT - 1];
+                    o[NPT - 1] = v[0];
+                } else if (j < 64) {
+#pragma unroll
+                    for (int h = 0; h < NPT; ++h) {
+                        const uint32_t lo = lane_xor((uint32_t)v[h], j), hi = lane_xor((uint32_t)(v[h] >> 32), j);
+                        o[h] = ((unsigned long long)hi << 32) | lo;
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < NPT; ++h) sh.list[tid + h * TK2_THREADS] = v[h];
+                    __syncthreads();
+#pragma unroll
+                    for (int h = 0; h < NPT; ++h) o[h] = sh.list[(tid + h * TK2_THREADS) ^ j];
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int h = 0; h < NPT; ++h) {
+                    const int p = tid + h * TK2_THREADS;
+                    // in a descending block of size k2 the lower place of a pair keeps the larger entry
+                    const bool keep_max = ((p & j) == 0) == ((p & k2) == 0);
+                    const bool larger = v[h] > o[h];
+                    v[h] = keep_max == larger ? v[h] : o[h];
+                }
             }
-        sh.list[q * 64 + lane] = v;   // the wave's own run: no other wave reads it before the barrier
-    }
-    __syncthreads();
-    for (int q = w; q < nrun; q += TK2_THREADS / 64) {
-        const unsigned long long e = sh.list[q * 64 + lane];
-        if (e == 0ull) continue;   // padding
-        uint32_t place = 0;
-        for (int r0 = 0; r0 < nrun; r0 += 8) {
-            int pos[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) pos[u] = 0;
-#pragma unroll
-            for (int step = 32; step >= 1; step >>= 1)
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (r0 + u < nrun && sh.list[(r0 + u) * 64 + pos[u] + step - 1] > e) pos[u] += step;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {   // the steps reach 63: a run wholly above e counts 64
-                if (r0 + u < nrun && sh.list[(r0 + u) * 64 + 63] > e) pos[u] = 64;
-                place += (uint32_t)pos[u];
+        for (int h = 0; h < NPT; ++h) {
+            const int place = tid + h * TK2_THREADS;
+            if (place < (int)k) {
+                const unsigned long long e = v[h];
+                const uint32_t low = (uint32_t)e;
+                const uint32_t f = 0x7ffffu - (low >> 13);
+                out_tok[(size_t)r * k_global + place] = sh.tok[low & 0x1fffu];
+                out_par[(size_t)r * k_global + place] = (int)(f / (uint32_t)k_local);
+                out_score[(size_t)r * k_global + place] = key32_value(e >> 32);
             }
         }
-        if (place < k) {
-            const uint32_t low = (uint32_t)e;
-            const uint32_t f = 0x7ffffu - (low >> 13);
-            out_tok[(size_t)r * k_global + place] = sh.tok[low & 0x1fffu];
-            out_par[(size_t)r * k_global + place] = (int)(f / (uint32_t)k_local);
-            out_score[(size_t)r * k_global + place] = key32_value(e >> 32);
-        }
-    }
+    };
+    if (m <= TK2_THREADS)
+        sort_and_store(std::integral_constant<int, TK2_THREADS>{});
+    else
+        sort_and_store(std::integral_constant<int, TK2_SORT>{});
 }
 
 // The library's own workspace for callers that cannot allocate device memory
