@@ -70,7 +70,7 @@ MEASURED_TRAFFIC: dict = {
     "short_decode/reorder": {"kernel": "suffix_reorder", "fetch_kib": 7693.0, "write_kib": 16024.9, "sources_sha256": "e0ef6d4301e3490d"},
     "long_beam/decode": {"kernel": "shared_prefix_decode", "fetch_kib": 34381.4, "write_kib": 15392.0, "sources_sha256": "6f5b3400c5b60814"},
     "long_beam/reorder": {"kernel": "suffix_reorder", "fetch_kib": 14329.8, "write_kib": 38460.5, "sources_sha256": "e0ef6d4301e3490d"},
-    "long_beam/topk": {"kernel": "beam_topk", "fetch_kib": 475898.1, "write_kib": 20037.5, "sources_sha256": "786fecead2b265f9"},
+    "long_beam/topk": {"kernel": "beam_topk", "fetch_kib": 475894.7, "write_kib": 20037.5, "sources_sha256": "5d5c523849b895fa"},
     "swiglu_fp8": {"kernel": "swiglu_quant", "fetch_kib": 33840.5, "write_kib": 17044.1, "sources_sha256": "58bd510a4b1ecb4f"},
 }
 
