@@ -48,7 +48,6 @@
 #pragma once
 
 #include <type_traits>
-#include <utility>
 
 #include "device_common.hpp"
 
@@ -69,14 +68,6 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t ld
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_dst)
                  : "memory", "m0");
-}
-// The same with the LDS address formed as lds_wave + C in the M0 write itself
-// (C a compile-time byte offset): one scalar instruction per copy for it.
-template <uint32_t C>
-__device__ __forceinline__ void dma16_at(uint64_t sbase, uint32_t voff, uint32_t lds_wave)
-{
-    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase),
-                 "s"(lds_wave), "n"(C) : "memory", "m0");
 }
 
 // a wave-uniform 64-bit value kept in scalar registers
@@ -130,7 +121,7 @@ struct Copier {
     static constexpr int N = G::DMA / NW;   // copies per wave per tile
     static_assert(G::DMA % NW == 0, "copies must split evenly over the waves");
     static_assert((NW * G::RPI) % 16 == 0, "copy stride must keep the swizzle");
-    uint32_t koff, voff;   // per-lane byte offset of this wave's first copy of a whole tile (row, swizzled chunk)
+    uint32_t koff, voff;   // per-lane byte offset of a full tile's copy (row within copy, swizzled chunk)
     uint32_t kch, vch;     // swizzled chunk byte offsets
     int lrow;              // lane's row within its copy
     int wave;              // wave-uniform
@@ -145,8 +136,8 @@ struct Copier {
         const int pc = lane % G::CHUNKS, row0 = wave * G::RPI + lrow;
         kch = (uint32_t)((pc ^ G::swk(row0)) * 16);
         vch = (uint32_t)((pc ^ G::swv(row0)) * 16);
-        koff = (uint32_t)row0 * rbytes + kch;
-        voff = (uint32_t)row0 * rbytes + vch;
+        koff = (uint32_t)lrow * rbytes + kch;
+        voff = (uint32_t)lrow * rbytes + vch;
     }
 
     // Copy the 64 rows starting at global byte address `tile` into the slot at
@@ -166,7 +157,7 @@ struct Copier {
 #pragma unroll
             for (int j = 0; j < N; ++j) {
                 const int i = wave + j * NW;
-                dma16(tile + (uint32_t)(j * NW * G::RPI) * rbytes, off, slot + (uint32_t)(i * 1024));
+                dma16(tile + (uint32_t)(i * G::RPI) * rbytes, off, slot + (uint32_t)(i * 1024));
             }
         } else {
 #pragma unroll
@@ -176,24 +167,6 @@ struct Copier {
                 dma16(tile, (uint32_t)r * rbytes + ch, slot + (uint32_t)(i * 1024));
             }
         }
-    }
-
-    // A whole tile (all 64 rows valid) into the slot at LDS byte offset SLOT from
-    // the workgroup's LDS base; lds_wave = that base + 1 KB * wave (uniform). No
-    // row clamping and the slot offset folded into the M0 writes: the scan's
-    // steady state issues its copies with a few scalar instructions.
-    template <bool IS_V, uint32_t SLOT>
-    __device__ __forceinline__ void issue_whole(uint64_t tile, uint32_t lds_wave) const
-    {
-        const uint32_t off = IS_V ? voff : koff;
-        asm volatile("" : "+s"(tile));
-        whole_copies<SLOT>(tile, off, lds_wave, std::make_integer_sequence<int, N>{});
-    }
-    template <uint32_t SLOT, int... J>
-    __device__ __forceinline__ void whole_copies(uint64_t tile, uint32_t off, uint32_t lds_wave,
-                                                 std::integer_sequence<int, J...>) const
-    {
-        (dma16_at<SLOT + (uint32_t)(J * NW * 1024)>(tile + (uint32_t)(J * NW * G::RPI) * rbytes, off, lds_wave), ...);
     }
 };
 
@@ -563,35 +536,21 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
     // Tile kt: K(kt) and V(kt) sit in slot kt & 1. Every tile starts with a
     // barrier after which K(kt+2) and V(kt+1) are copied into the slots that
     // K(kt) and V(kt-1) held (V(1) came with the first copies).
-    const uint32_t lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_base + (uint32_t)cp.wave * 1024u));
-    auto sync_and_copy = [&](int kt, auto parity) {
-        constexpr uint32_t p = decltype(parity)::value;   // kt & 1
+    auto sync_and_copy = [&](int kt) {
         wait_copies_and_sync();   // K(kt+1), V(kt) landed; K(kt), V(kt-1) no longer read
-        if (kt >= 1 && kt + 3 < nkt) {
-            // steady state: both tiles are whole (neither is the last one)
-            cp.template issue_whole<false, p * G::KBYTES>(kbase + (uint64_t)(kt + 2) * tile_bytes, lds_wave);
-            cp.template issue_whole<true, G::vslot(0) + (1 - p) * G::KBYTES>(vbase + (uint64_t)(kt + 1) * tile_bytes,
-                                                                           lds_wave);
-        } else {
-            if (kt + 2 < nkt)
-                cp.template issue<false>(lds_base + p * G::KBYTES, kbase + (uint64_t)(kt + 2) * tile_bytes,
-                                         last_row(kt + 2));
-            if (kt >= 1 && kt + 1 < nkt)
-                cp.template issue<true>(lds_base + G::vslot(0) + (1 - p) * G::KBYTES,
-                                        vbase + (uint64_t)(kt + 1) * tile_bytes, last_row(kt + 1));
-        }
+        const uint32_t p = (uint32_t)(kt & 1);
+        if (kt + 2 < nkt)
+            cp.template issue<false>(lds_base + p * G::KBYTES, kbase + (uint64_t)(kt + 2) * tile_bytes,
+                                     last_row(kt + 2));
+        if (kt >= 1 && kt + 1 < nkt)
+            cp.template issue<true>(lds_base + G::vslot(0) + (1 - p) * G::KBYTES,
+                                    vbase + (uint64_t)(kt + 1) * tile_bytes, last_row(kt + 1));
         extra(kt);
-    };
-    auto sync_and_copy_any = [&](int kt) {
-        if ((kt & 1) == 0)
-            sync_and_copy(kt, std::integral_constant<uint32_t, 0>{});
-        else
-            sync_and_copy(kt, std::integral_constant<uint32_t, 1>{});
     };
     // all but the wave's last tile: exponentials and P*V of tile kt, scores of kt+1
     auto step = [&](int kt, auto parity, f32x16(&sc)[2], f32x16(&sn)[2]) {
         constexpr int P = decltype(parity)::value;
-        sync_and_copy(kt, std::integral_constant<uint32_t, (uint32_t)P>{});
+        sync_and_copy(kt);
         float mx = st.step(rd, qop, sc, sn, G::kslot(1 - P), G::vslot(P), c2);
         if (kt + 1 >= kt_mask) {   // the next tile has keys past some row's limit
             Wave<D>::mask(sn, lim - (kt + 1) * G::BN);
@@ -611,7 +570,7 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
     }
     // the wave's last tile
     if (kt == klast) {
-        sync_and_copy_any(kt);
+        sync_and_copy(kt);
         if ((kt & 1) == 0)
             st.last(rd, sa, G::vslot(0), c2);
         else
@@ -619,7 +578,7 @@ __device__ __forceinline__ void scan(Wave<D> &st, const Reads<D> &rd, const Copi
         ++kt;
     }
     // the workgroup's remaining tiles: copies and barriers only
-    for (; kt < nkt; ++kt) sync_and_copy_any(kt);
+    for (; kt < nkt; ++kt) sync_and_copy(kt);
 }
 
 // Q^T operand of one lane: query row `qrow` (D elements), k slots (lane>>5)*8 + [0,8)
