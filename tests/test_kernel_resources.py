@@ -7,6 +7,11 @@ per CU (at most 128); the only scratch use is a few values kept across the d 64
 prefill and d 128 decode scans. A change that pushes a kernel past its budget
 halves its occupancy or moves values to scratch memory, which the GPU tests
 would not flag; this test does, from the compiler's own kernel descriptors.
+
+The K/V copies of the attention kernels write M0 inside inline assembly. The
+compiler treats M0 as a reserved register and does not promise to keep a value
+of its own there across such a statement, so the attention kernels' device code
+must not use M0 anywhere else; the last test checks that too.
 """
 import importlib.util
 import os
@@ -51,11 +56,12 @@ def descriptors(tmp_path_factory):
         cmd = [hipcc, *b.HIPCC_FLAGS, *b.PER_FILE_FLAGS.get(src, []), "--cuda-device-only", "-S",
                os.path.join(CSRC, src), "-o", dst]
         procs.append((src, dst, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
-    desc = {}
+    desc, asm = {}, {}
     for src, dst, p in procs:
         log, _ = p.communicate()
         assert p.returncode == 0, f"{src}: {log[-2000:]}"
         text = open(dst).read()
+        asm[src] = text
         # the code-object metadata lists every kernel with its resource counts
         for blk in re.split(r"\n  - \.", text.split("amdhsa.kernels:", 1)[1]):
             name = re.search(r"\.name:\s+(\S+)", blk)
@@ -63,14 +69,27 @@ def descriptors(tmp_path_factory):
             scratch = re.search(r"\.private_segment_fixed_size:\s+(\d+)", blk)
             if name and vgpr and scratch:
                 desc[name.group(1)] = (int(vgpr.group(1)), int(scratch.group(1)))
-    return desc
+    return desc, asm
 
 
 @pytest.mark.parametrize("prefix", sorted(BUDGETS))
 def test_kernel_stays_within_its_budget(descriptors, prefix):
-    found = {n: v for n, v in descriptors.items() if n.startswith(prefix)}
+    found = {n: v for n, v in descriptors[0].items() if n.startswith(prefix)}
     assert found, f"no kernel named {prefix}* in the device code"
     _, max_vgpr, max_scratch = BUDGETS[prefix]
     for name, (vgpr, scratch) in found.items():
         assert vgpr <= max_vgpr, f"{name}: {vgpr} VGPRs > {max_vgpr}"
         assert scratch <= max_scratch, f"{name}: {scratch} bytes of scratch per lane > {max_scratch}"
+
+
+@pytest.mark.parametrize("src", ["prefill.hip", "decode.hip"])
+def test_m0_is_written_only_by_the_copy_statements(descriptors, src):
+    inside, uses = False, []
+    for line in descriptors[1][src].splitlines():
+        if ";;#ASMSTART" in line:
+            inside = True
+        elif ";;#ASMEND" in line:
+            inside = False
+        elif not inside and not line.lstrip().startswith((";", ".")) and re.search(r"\bm0\b", line):
+            uses.append(line.strip())
+    assert uses == [], f"{src}: the compiler uses M0 outside the copy statements: {uses[:3]}"
