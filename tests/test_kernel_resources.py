@@ -93,3 +93,23 @@ def test_m0_is_written_only_by_the_copy_statements(descriptors, src):
         elif not inside and not line.lstrip().startswith((";", ".")) and re.search(r"\bm0\b", line):
             uses.append(line.strip())
     assert uses == [], f"{src}: the compiler uses M0 outside the copy statements: {uses[:3]}"
+
+
+# scalar instructions that write SCC; none may sit inside inline assembly (see
+# tests/test_inline_asm.py for why), checked here on the compiler's output too
+_SCC_WRITER = re.compile(r"^\s*s_(cmp\w*|add_[iu]32|sub_[iu]32|addc_u32|subb_u32|addk_i32|and_\w+|or_\w+|xor_\w+|"
+                         r"andn2_\w+|orn2_\w+|nand_\w+|nor_\w+|xnor_\w+|lshl\w*|lshr\w*|ashr\w*|bfe_\w+|min_\w+|"
+                         r"max_\w+|abs\w*|not_\w+|bitcmp\w*|bcnt\w*|absdiff_\w+)\b")
+
+
+@pytest.mark.parametrize("src", sorted({v[0] for v in BUDGETS.values()}))
+def test_compiled_inline_asm_writes_no_scc(descriptors, src):
+    inside, bad = False, []
+    for line in descriptors[1][src].splitlines():
+        if ";;#ASMSTART" in line:
+            inside = True
+        elif ";;#ASMEND" in line:
+            inside = False
+        elif inside and _SCC_WRITER.match(line):
+            bad.append(line.strip())
+    assert bad == [], f"{src}: inline assembly writes SCC: {bad[:3]}"
